@@ -1,0 +1,377 @@
+"""Pins for the CPU oracle: facts the pages print, closed forms, special cases,
+brute force on tiny inputs and library routines.  CPU only.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+sign, a transposed operand, a wrong tie order, a wrong half of the merged
+gate_up tensor) makes at least one of them fail.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits(a):
+    return mi.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def _random_layer(dims, seed, std=0.02):
+    return mi.make_layer(dims, seed, std=std)
+
+
+# ---------------------------------------------------------------------------
+# Figures the pages print.
+# ---------------------------------------------------------------------------
+
+def _golden_counts():
+    rows = {}
+    with open(os.path.join(GOLDEN, "param_counts.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, value, digits, _src = [c.strip() for c in line.split("|", 3)]
+            rows[name] = (value, digits)
+    return rows
+
+
+def _round_sig(v, d):
+    return float(f"{v:.{d - 1}e}")
+
+
+def test_param_counts_match_printed_figures():
+    g = _golden_counts()
+    d = mi.FULL
+    per_expert = O.expert_param_count(d.H, d.I)
+    assert per_expert == 3 * 2048 * 512 == 3_145_728
+    for key in ("expert_params_p1", "expert_params_p2"):
+        value, digits = g[key]
+        assert _round_sig(per_expert, int(digits)) == float(value)
+    value, digits = g["active_expert_params"]
+    assert _round_sig(d.K * per_expert, int(digits)) == float(value)
+    # "806M total": the routed experts alone give 805.3M; with the router
+    # (256 x 2048) the printed 806M is reproduced, so the figure includes it.
+    value, digits = g["total_expert_params"]
+    routed = d.E * per_expert
+    assert _round_sig(routed, int(digits)) != float(value)
+    assert _round_sig(routed + d.E * d.H, int(digits)) == float(value)
+    shapes = d.shapes()
+    assert shapes["gate_up_proj"] == tuple(int(v) for v in g["merged_gate_up_shape"][0].split(","))
+    assert shapes["down_proj"] == tuple(int(v) for v in g["down_shape"][0].split(","))
+    assert shapes["gate.weight"] == tuple(int(v) for v in g["router_shape"][0].split(","))
+    assert d.K == int(g["top_k"][0])
+
+
+# ---------------------------------------------------------------------------
+# bf16 codec (IEEE facts).
+# ---------------------------------------------------------------------------
+
+def test_bf16_decode_known_patterns():
+    cases = {
+        0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x4049: 3.140625, 0x3C23: 0.0099487305,
+        0x0000: 0.0, 0x7F7F: 3.3895313892515355e38, 0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133,
+    }
+    got = O.bf16_to_f64(np.array(list(cases), dtype=np.uint16))
+    for (bits, want), g in zip(cases.items(), got):
+        assert g == pytest.approx(want, rel=1e-7, abs=0), hex(bits)
+    assert math.copysign(1.0, O.bf16_to_f64(np.array([0x8000], np.uint16))[0]) == -1.0
+
+
+def test_bf16_encoder_rounds_to_nearest_even():
+    # 1 + 2^-8 is half way between 1 and 1 + 2^-7: ties go to the even pattern 0x3F80.
+    v = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -2.5], np.float32)
+    assert list(_bits(v)) == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020]
+    r = np.random.default_rng(0).standard_normal(1000).astype(np.float32)
+    back = O.bf16_to_f64(_bits(r))
+    assert np.all(np.abs(back - r) <= np.abs(r) * 2.0 ** -8)
+
+
+# ---------------------------------------------------------------------------
+# Activations: closed forms and a library implementation.
+# ---------------------------------------------------------------------------
+
+def test_activation_closed_forms():
+    assert O.sigmoid(0.0) == 0.5
+    assert O.silu(0.0) == 0.0
+    assert O.sigmoid(math.log(3.0)) == pytest.approx(0.75, rel=1e-15)
+    assert O.silu(math.log(3.0)) == pytest.approx(0.75 * math.log(3.0), rel=1e-15)
+    assert O.sigmoid(800.0) == 1.0 and O.sigmoid(-800.0) == 0.0
+    assert O.silu(-800.0) == 0.0 and O.silu(800.0) == 800.0
+    z = np.random.default_rng(1).standard_normal(4096) * 6
+    t = torch.from_numpy(z)
+    np.testing.assert_allclose(O.silu(z), torch.nn.functional.silu(t).numpy(), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(O.sigmoid(z), torch.sigmoid(t).numpy(), rtol=1e-14, atol=1e-300)
+
+
+# ---------------------------------------------------------------------------
+# Router: brute-force dot products.
+# ---------------------------------------------------------------------------
+
+def test_router_logits_brute_force():
+    rng = np.random.default_rng(2)
+    x = _bits(rng.standard_normal((3, 8)))
+    w = _bits(rng.standard_normal((5, 8)) * 0.02)
+    xf, wf = O.bf16_to_f64(x), O.bf16_to_f64(w)
+    want = np.array([[math.fsum(xf[t, h] * wf[e, h] for h in range(8)) for e in range(5)] for t in range(3)])
+    np.testing.assert_allclose(O.router_logits(x, w), want, rtol=1e-15, atol=1e-18)
+
+
+# ---------------------------------------------------------------------------
+# Ranks / top-K / renormalisation.
+# ---------------------------------------------------------------------------
+
+def _brute_topk(l, K):
+    order = sorted(range(len(l)), key=lambda e: (-l[e], e))
+    return order[:K], {e: r for r, e in enumerate(order)}
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    E, K = 12, 4
+    # Integer-valued logits produce many exact ties.
+    logits = rng.integers(-3, 4, size=(20, E)).astype(np.float64)
+    logits[0] = 0.0
+    idx, w = O.select_topk(logits, K)
+    r = O.ranks(logits)
+    for t in range(logits.shape[0]):
+        want_idx, want_rank = _brute_topk(list(logits[t]), K)
+        assert list(idx[t]) == want_idx
+        assert [r[t, e] for e in range(E)] == [want_rank[e] for e in range(E)]
+        # Weights: softmax over only the selected logits is the same quantity.
+        sel = logits[t, want_idx]
+        ref = np.exp(sel - sel.max())
+        np.testing.assert_allclose(w[t], ref / ref.sum(), rtol=1e-13)
+    assert list(idx[0]) == [0, 1, 2, 3]
+
+
+def test_topk_invariants_on_toy_workload():
+    wl = mi.WORKLOADS["toy"]
+    layer = mi.workload_layer(wl)
+    x = mi.workload_x(wl)
+    R = O.route(x, layer, wl.dims.K)
+    idx, w = R["topk_idx"], R["topk_w"]
+    assert idx.shape == (wl.T, wl.dims.K) and idx.dtype == np.int32
+    assert np.all((idx >= 0) & (idx < wl.dims.E))
+    assert all(len(set(row)) == wl.dims.K for row in idx)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(np.diff(w, axis=1) <= 0)
+    sel_logits = np.take_along_axis(R["logits"], idx.astype(np.int64), axis=1)
+    assert np.all(np.diff(sel_logits, axis=1) <= 0)
+    # Everything not selected scores no higher than the K-th selected logit.
+    for t in range(wl.T):
+        rest = np.delete(R["logits"][t], idx[t])
+        assert rest.max() <= sel_logits[t, -1]
+
+
+def test_topk_special_cases():
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((7, 16))
+    # K = E: the renormalised weights are the plain softmax over all experts.
+    idx, w = O.select_topk(logits, 16)
+    full = scipy.special.softmax(logits, axis=1)
+    np.testing.assert_allclose(np.take_along_axis(full, idx.astype(np.int64), axis=1), w, rtol=1e-13)
+    # K = 1: the single weight is exactly 1 and the index is the argmax.
+    idx1, w1 = O.select_topk(logits, 1)
+    assert np.all(w1 == 1.0) and np.array_equal(idx1[:, 0], np.argmax(logits, axis=1))
+    # x = 0: all logits tie, every token is flagged, experts 0..K-1 with weight 1/K.
+    d = mi.TOY
+    layer = _random_layer(d, 5)
+    x0 = np.zeros((4, d.H), np.uint16)
+    R = O.route(x0, layer, d.K)
+    assert np.all(R["topk_idx"] == np.arange(d.K)) and np.allclose(R["topk_w"], 1.0 / d.K)
+    assert R["tie"].all()
+
+
+def test_tie_flags_boundaries():
+    K = 3
+    base = np.array([5.0, 4.0, 3.0, 2.0, 1.0, 0.0])
+    rows = [base.copy() for _ in range(5)]
+    rows[1][1] = 5.0 - 5e-7          # gap inside the top-K
+    rows[2][3] = 3.0 - 5e-7          # gap across the K / K+1 boundary
+    rows[3][4] = 2.0 - 5e-7          # gap below rank K+1 only: harmless
+    rows[4][3] = 3.0 - 2e-6          # gap across the boundary but above 1e-6
+    flags = O.tie_flags(np.array(rows)[:, ::-1].copy(), K)   # order of columns is irrelevant
+    assert list(flags) == [False, True, True, False, False]
+
+
+# ---------------------------------------------------------------------------
+# Counting sort.
+# ---------------------------------------------------------------------------
+
+def _loop_counting_sort(topk_idx, E):
+    """Textbook counting sort written out with loops: histogram, scan, cursor scatter."""
+    keys = [int(v) for v in np.asarray(topk_idx).reshape(-1)]
+    counts = [0] * E
+    for k in keys:
+        counts[k] += 1
+    offsets = [0] * (E + 1)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:E]
+    perm = [0] * len(keys)
+    for q, k in enumerate(keys):
+        perm[cursor[k]] = q
+        cursor[k] += 1
+    return counts, offsets, perm
+
+
+@pytest.mark.parametrize("T,E,K,mode", [(8, 16, 4, "random"), (37, 16, 4, "random"),
+                                        (64, 256, 8, "random"), (50, 16, 4, "same"),
+                                        (0, 16, 4, "random"), (1, 256, 8, "random")])
+def test_counting_sort_brute_force(T, E, K, mode):
+    rng = np.random.default_rng(T * 31 + E)
+    if mode == "same":
+        idx = np.tile(np.array([3, 0, 15, 7], np.int32), (T, 1))
+    else:
+        idx = np.array([rng.permutation(E)[:K] for _ in range(T)], dtype=np.int32).reshape(T, K)
+    d = O.counting_sort(idx, E)
+    counts, offsets, perm = _loop_counting_sort(idx, E)
+    assert list(d["counts"]) == counts and list(d["offsets"]) == offsets and list(d["perm"]) == perm
+    assert d["offsets"][E] == T * K and np.all(np.diff(d["offsets"]) >= 0)
+    assert np.array_equal(np.sort(d["perm"]), np.arange(T * K))
+    assert np.array_equal(d["perm"][d["slot_of"]], np.arange(T * K))
+    for e in range(E):
+        seg = d["perm"][d["offsets"][e]:d["offsets"][e + 1]]
+        assert np.all(idx.reshape(-1)[seg] == e)
+        assert np.all(np.diff(seg // K) > 0)     # strictly increasing token within a segment
+
+
+# ---------------------------------------------------------------------------
+# The whole layer.
+# ---------------------------------------------------------------------------
+
+def test_hand_worked_example():
+    with open(os.path.join(GOLDEN, "hand_example.json")) as f:
+        g = json.load(f)
+    params = {k: _bits(g[k]) for k in mi.PARAM_NAMES}
+    x = _bits(g["x"])
+    K = g["dims"]["K"]
+    sig = lambda z: 1.0 / (1.0 + math.exp(-z))   # noqa: E731
+    closed = [4 * sig(1) * sig(2) + 2 * sig(-1) * sig(2) - 1.5 * sig(1) * sig(-1),
+              -4 * sig(1) * sig(2) + 0.5 * sig(-1) * sig(2) - 3 * sig(1) * sig(-1)]
+    np.testing.assert_allclose(g["out"], closed, rtol=1e-15)
+    R = O.route(x, params, K)
+    assert R["topk_idx"].tolist() == g["topk_idx"]
+    np.testing.assert_allclose(R["topk_w"][0], [sig(1), sig(-1)], rtol=1e-15)
+    np.testing.assert_allclose(O.forward(x, params, K)[0], closed, rtol=1e-14)
+    np.testing.assert_allclose(O.forward_dense(x, params, K)[0], closed, rtol=1e-14)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_sparse_equals_dense_brute_force(seed):
+    d = mi.TOY
+    layer = _random_layer(d, 10 + seed)
+    x = mi.make_x(d, 8 if seed else mi.WORKLOADS["toy"].T, 20 + seed)
+    sparse = O.forward(x, layer, d.K)
+    dense = O.forward_dense(x, layer, d.K)
+    np.testing.assert_allclose(sparse, dense, rtol=1e-12, atol=1e-15)
+
+
+def _torch_swiglu(X, wg, wu, wd):
+    X = torch.from_numpy(X)
+    return (torch.nn.functional.silu(X @ torch.from_numpy(wg).T) * (X @ torch.from_numpy(wu).T)
+            @ torch.from_numpy(wd).T).numpy()
+
+
+def test_identical_experts_reduce_to_one_swiglu():
+    # With every routed expert equal, the weights summing to one make the routed
+    # part a single dense SwiGLU whatever the routing is.
+    d = mi.TOY
+    layer = _random_layer(d, 30)
+    layer["gate_up_proj"] = np.repeat(layer["gate_up_proj"][:1], d.E, axis=0)
+    layer["down_proj"] = np.repeat(layer["down_proj"][:1], d.E, axis=0)
+    x = mi.make_x(d, 11, 31)
+    X = O.bf16_to_f64(x)
+    gu = O.bf16_to_f64(layer["gate_up_proj"][0])
+    routed = _torch_swiglu(X, gu[:d.I], gu[d.I:], O.bf16_to_f64(layer["down_proj"][0]))
+    s = torch.sigmoid(torch.from_numpy(X @ O.bf16_to_f64(layer["shared_expert_gate.weight"]).T)).numpy()
+    shared = _torch_swiglu(X, O.bf16_to_f64(layer["shared_expert.gate.weight"]),
+                           O.bf16_to_f64(layer["shared_expert.up.weight"]),
+                           O.bf16_to_f64(layer["shared_expert.down.weight"]))
+    np.testing.assert_allclose(O.forward(x, layer, d.K), routed + s * shared, rtol=1e-11, atol=1e-14)
+    # The merged tensor's halves are not interchangeable: swapping gate and up changes the result.
+    swapped = dict(layer)
+    swapped["gate_up_proj"] = np.concatenate([layer["gate_up_proj"][:, d.I:], layer["gate_up_proj"][:, :d.I]], axis=1)
+    assert not np.allclose(O.forward(x, swapped, d.K), O.forward(x, layer, d.K), rtol=1e-3)
+
+
+def test_zero_weight_special_cases():
+    d = mi.TOY
+    layer = _random_layer(d, 40)
+    x = mi.make_x(d, 9, 41)
+    X = O.bf16_to_f64(x)
+    shared = _torch_swiglu(X, O.bf16_to_f64(layer["shared_expert.gate.weight"]),
+                           O.bf16_to_f64(layer["shared_expert.up.weight"]),
+                           O.bf16_to_f64(layer["shared_expert.down.weight"]))
+    # Zero routed down weights leave only the gated shared expert.
+    z = dict(layer, down_proj=np.zeros_like(layer["down_proj"]))
+    s = 1 / (1 + np.exp(-(X @ O.bf16_to_f64(layer["shared_expert_gate.weight"]).T)))
+    np.testing.assert_allclose(O.forward(x, z, d.K), s * shared, rtol=1e-12, atol=1e-15)
+    # A zero shared-gate row gives a gate of exactly one half.
+    z2 = dict(z, **{"shared_expert_gate.weight": np.zeros_like(layer["shared_expert_gate.weight"])})
+    np.testing.assert_allclose(O.forward(x, z2, d.K), 0.5 * shared, rtol=1e-12, atol=1e-15)
+    # x = 0 gives an output of exactly zero.
+    assert np.all(O.forward(np.zeros_like(x), layer, d.K) == 0.0)
+
+
+def test_token_permutation_and_subsets():
+    d = mi.TOY
+    layer = _random_layer(d, 50)
+    x = mi.make_x(d, 13, 51)
+    out = O.forward(x, layer, d.K)
+    p = np.random.default_rng(52).permutation(13)
+    np.testing.assert_allclose(O.forward(x[p], layer, d.K), out[p], rtol=1e-12, atol=1e-15)
+    # Tokens do not interact: the output of a subset is the subset of the output.
+    sub = np.array([0, 5, 12])
+    np.testing.assert_allclose(O.forward(x[sub], layer, d.K), out[sub], rtol=1e-12, atol=1e-15)
+
+
+def test_forward_with_routing_matches_own_choice():
+    d = mi.TOY
+    layer = _random_layer(d, 60)
+    x = mi.make_x(d, 10, 61)
+    R = O.route(x, layer, d.K)
+    np.testing.assert_allclose(O.forward_with_routing(x, layer, R["topk_idx"]),
+                               O.forward(x, layer, d.K), rtol=1e-13, atol=1e-16)
+    # Order of the chosen experts does not matter to the output.
+    np.testing.assert_allclose(O.forward_with_routing(x, layer, R["topk_idx"][:, ::-1].copy()),
+                               O.forward(x, layer, d.K), rtol=1e-13, atol=1e-16)
+
+
+def test_all_k_and_e_combinations_small():
+    # Brute force over small shapes, including K = E (every expert selected).
+    for E, K in itertools.product([4, 8], [1, 2, 4]):
+        d = mi.Dims(H=16, E=E, K=K, I=4, Is=4)
+        layer = _random_layer(d, 70 + E + K, std=0.3)
+        x = mi.make_x(d, 5, 80 + E)
+        np.testing.assert_allclose(O.forward(x, layer, K), O.forward_dense(x, layer, K), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Skewed-load workload: the fitted router gives the intended load profile.
+# ---------------------------------------------------------------------------
+
+def test_zipf_workload_is_skewed():
+    wl = mi.WORKLOADS["zipf16384"]
+    gain = mi.zipf_router_gain()
+    assert gain.shape == (wl.dims.E,) and np.all(gain > 0)
+    router = mi.make_layer(mi.Dims(H=wl.dims.H, E=wl.dims.E, K=wl.dims.K, I=1, Is=1), wl.layer_seed,
+                           router_row_gain=gain)["gate.weight"]
+    # The router tensor of the workload is the same draw with the gain applied.
+    x = mi.workload_x(wl)
+    idx, _ = O.select_topk(O.router_logits(x, router), wl.dims.K)
+    load = np.bincount(idx.reshape(-1), minlength=wl.dims.E)
+    mean = wl.T * wl.dims.K / wl.dims.E
+    assert load.sum() == wl.T * wl.dims.K
+    assert load.max() >= 10 * mean
+    assert load.max() <= 0.5 * wl.T          # an expert cannot win more than about half the tokens
