@@ -1,0 +1,125 @@
+/*
+ * moe.h — C ABI of the sparse mixture-of-experts FFN layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (Qwen3.6-35B-A3B MoE FFN), as defined by "Qwen3.6-35B-A3B —
+ * Architecture Overview" (Hugging Face blog), section "MoE FFN: 256 Experts",
+ * with the tensor shapes of the Linnet model page "Qwen3.6 35B-A3B",
+ * Blocks: SparseMoe, SwiGlu, Linear:
+ *
+ *   logits[t, e] = x[t] . router_w[e]                              (router)
+ *   top-K experts per token by logit (ties: lower expert index first),
+ *   w[t, k]      = softmax(logits[t])[e_k] / sum_j softmax(logits[t])[e_j]
+ *   expert_e(v)  = (SiLU(v Wg_e^T) * (v Wu_e^T)) Wd_e^T,
+ *                  Wg_e = gate_up_w[e, 0:I, :], Wu_e = gate_up_w[e, I:2I, :],
+ *                  Wd_e = down_w[e]
+ *   out[t]       = sum_k w[t, k] expert_{e_k}(x[t])
+ *                + sigmoid(x[t] . shared_expert_gate_w) * shared(x[t])
+ *
+ * with shared(v) the same SwiGLU over shared_gate_w / shared_up_w /
+ * shared_down_w (inner size Is).  No biases, no residual, no norm: out is the
+ * MoE block's output alone.  Every (token, expert) pair is computed (no
+ * capacity limit).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense row-major bf16 (uint16 bit patterns of bfloat16) unless
+ *    stated; a Linear weight is stored [Out, In].  Device pointers are owned
+ *    by the caller; the library keeps none of them after a call returns and
+ *    allocates no device memory.
+ *  - Every device pointer must be 16-byte aligned.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  The caller must keep x, out, the weights and the workspace
+ *    alive and unmodified until the stream work has completed.  Calls that
+ *    share a workspace must be ordered on one stream.
+ *  - Results are bitwise reproducible from run to run on the same device.
+ *  - Return value: MOE_OK or one of the MOE_ERR_* codes below.  All argument
+ *    checks run before any HIP call; then nothing has been enqueued.
+ *    moe_last_error() gives a per-thread text for the last failure.
+ *  - Inputs are assumed finite; NaN/Inf in x or the weights give unspecified
+ *    routing.
+ *
+ * Supported dimensions: H % 256 == 0, I % 64 == 0, Is % 64 == 0,
+ * 1 <= K <= 8, K <= E <= 256, 0 <= T <= 2^22.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  MOE_ERR_SHAPE = 2,     /* T < 0, K/E/H/I/Is outside the supported set         */
+  MOE_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned             */
+  MOE_ERR_WORKSPACE = 4, /* ws_bytes < moe_workspace_bytes(L, T)                */
+  MOE_ERR_DEVICE = 5,    /* the current HIP device is not a gfx950              */
+  MOE_ERR_LAUNCH = 6     /* a HIP call failed; moe_last_error() has its text    */
+};
+
+/* One MoE layer: dimensions and device pointers to its seven parameters
+ * (Linnet page, Blocks: SparseMoe members gate, gate_up_proj, down_proj,
+ * shared_expert {gate, up, down}, shared_expert_gate). */
+typedef struct moe_layer {
+  int32_t hidden;        /* H                                                    */
+  int32_t num_experts;   /* E                                                    */
+  int32_t top_k;         /* K                                                    */
+  int32_t expert_inner;  /* I                                                    */
+  int32_t shared_inner;  /* Is                                                   */
+  const void *router_w;             /* bf16 [E, H]      gate.weight                */
+  const void *gate_up_w;            /* bf16 [E, 2I, H]  rows [0,I) gate, [I,2I) up */
+  const void *down_w;               /* bf16 [E, H, I]   down_proj                  */
+  const void *shared_gate_w;        /* bf16 [Is, H]     shared_expert.gate.weight  */
+  const void *shared_up_w;          /* bf16 [Is, H]     shared_expert.up.weight    */
+  const void *shared_down_w;        /* bf16 [H, Is]     shared_expert.down.weight  */
+  const void *shared_expert_gate_w; /* bf16 [1, H]      shared_expert_gate.weight  */
+} moe_layer_t;
+
+/* Bytes of device workspace that moe_route / moe_forward need for T tokens
+ * (0 for T <= 0 or unsupported dimensions).  Host-only; no HIP call. */
+size_t moe_workspace_bytes(const moe_layer_t *L, int64_t T);
+
+/* Check the arguments of a moe_forward call without touching the GPU.
+ * Returns the code moe_forward would return before its first HIP call. */
+int moe_validate(const moe_layer_t *L, const void *x, int64_t T, const void *out,
+                 const void *ws, size_t ws_bytes);
+
+/* Routing and dispatch only (router, softmax, top-K, renormalise, the
+ * shared-expert gate scalar, and the stable grouping of (token, k) pairs by
+ * expert).  Same kernels and results as inside moe_forward.
+ *   x         bf16 [T, H]
+ *   topk_idx  int32 [T, K]  selected experts in rank order (descending logit,
+ *                           ties to the lower expert index)
+ *   topk_w    fp32 [T, K]   renormalised routing weights (sum to 1 per token)
+ *   offsets   int32 [E+1]   segment starts: pairs of expert e occupy slots
+ *                           offsets[e] .. offsets[e+1]-1; offsets[E] = T*K
+ *   perm      int32 [T*K]   pair id q = t*K + k held by each slot, ascending
+ *                           t within a segment
+ *   shared_gate fp32 [T] or NULL   sigmoid(x[t] . shared_expert_gate_w)
+ *   logits    fp32 [T, E] or NULL  router logits (fp32 accumulation)
+ * T = 0 is a successful no-op. */
+int moe_route(const moe_layer_t *L, const void *x, int64_t T,
+              int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *perm,
+              float *shared_gate, float *logits,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer: out bf16 [T, H] (round to nearest even from an fp32
+ * accumulation).  x and out must not overlap.  T = 0 is a successful no-op. */
+int moe_forward(const moe_layer_t *L, const void *x, int64_t T, void *out,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *moe_strerror(int code);
+
+/* Text describing the last failure on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

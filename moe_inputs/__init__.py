@@ -149,6 +149,12 @@ def make_layer(dims: Dims, seed: int, std: float = WEIGHT_STD,
     return layer
 
 
+def make_router(dims: Dims, seed: int, router_row_gain: np.ndarray | None = None,
+                std: float = WEIGHT_STD) -> np.ndarray:
+    """Only the router weight [E, H] of ``make_layer(dims, seed, ...)`` (same draw)."""
+    return _normal_bf16(seed, "gate.weight", (dims.E, dims.H), std, gain=router_row_gain)
+
+
 def make_x(dims: Dims, T: int, seed: int, std: float = 1.0) -> np.ndarray:
     """Hidden states x [T, H] as bf16 bits, std * N(0,1)."""
     return _normal_bf16(seed, "x", (int(T), dims.H), std)

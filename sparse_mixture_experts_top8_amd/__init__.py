@@ -1,0 +1,126 @@
+"""Sparse MoE FFN layer (256 experts, top-8, gated shared expert) on MI355X.
+
+Python face of the gfx950 HIP library: the layer of "Qwen3.6-35B-A3B —
+Architecture Overview", section "MoE FFN: 256 Experts", with the parameter
+shapes of the Linnet model page "Qwen3.6 35B-A3B" (Blocks: SparseMoe).
+
+    layer = MoeLayer.from_bf16_bits(params_uint16, dims, device="cuda")
+    out = forward(x, layer)            # x: bf16 [T, H] on the GPU
+    r = route(x, layer)                # topk_idx, topk_w, offsets, perm, ...
+
+The functions only marshal arguments to the C ABI (include/moe.h); all work
+runs in the library's kernels on the caller's current HIP stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from ._lib import (EXPORTS, LIB_PATH, MoeError, MoeLayerT, lib, last_error,  # noqa: F401
+                   strerror)
+
+PARAM_NAMES = (
+    "gate.weight",
+    "gate_up_proj",
+    "down_proj",
+    "shared_expert.gate.weight",
+    "shared_expert.up.weight",
+    "shared_expert.down.weight",
+    "shared_expert_gate.weight",
+)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class MoeLayer:
+    """Device-resident parameters of one layer plus its C descriptor."""
+    H: int
+    E: int
+    K: int
+    I: int
+    Is: int
+    params: dict
+
+    def __post_init__(self):
+        p = self.params
+        for name in PARAM_NAMES:
+            t = p[name]
+            if t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+        self.desc = MoeLayerT(self.H, self.E, self.K, self.I, self.Is,
+                              _ptr(p["gate.weight"]), _ptr(p["gate_up_proj"]), _ptr(p["down_proj"]),
+                              _ptr(p["shared_expert.gate.weight"]), _ptr(p["shared_expert.up.weight"]),
+                              _ptr(p["shared_expert.down.weight"]), _ptr(p["shared_expert_gate.weight"]))
+
+    @classmethod
+    def from_bf16_bits(cls, bits: dict, H: int, E: int, K: int, I: int, Is: int, device="cuda"):
+        """Upload uint16 bf16 bit arrays (numpy) to the device as bfloat16 tensors."""
+        p = {n: bits_to_device(bits[n], device) for n in PARAM_NAMES}
+        return cls(H, E, K, I, Is, p)
+
+    def workspace_bytes(self, T: int) -> int:
+        return int(lib.moe_workspace_bytes(self.desc, int(T)))
+
+    def workspace(self, T: int, device=None) -> torch.Tensor:
+        dev = device or self.params["gate.weight"].device
+        return torch.empty(max(1, self.workspace_bytes(T)), dtype=torch.uint8, device=dev)
+
+
+def bits_to_device(bits, device="cuda") -> torch.Tensor:
+    """uint16 numpy array of bf16 bit patterns -> contiguous bfloat16 tensor on ``device``."""
+    import numpy as np
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).to(device).view(torch.bfloat16)
+
+
+def _check_x(x, layer):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != layer.H or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous bfloat16 [T, {layer.H}] tensor")
+
+
+def forward(x: torch.Tensor, layer: MoeLayer, out: torch.Tensor | None = None,
+            ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The MoE layer on the GPU: bf16 [T, H] -> bf16 [T, H]."""
+    _check_x(x, layer)
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if ws is None:
+        ws = layer.workspace(T, x.device)
+    rc = lib.moe_forward(layer.desc, _ptr(x), T, _ptr(out), _ptr(ws), ws.numel(), _stream_handle(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_forward")
+    return out
+
+
+def route(x: torch.Tensor, layer: MoeLayer, ws: torch.Tensor | None = None, stream=None,
+          want_logits: bool = False) -> dict:
+    """Routing and dispatch only; returns device tensors."""
+    _check_x(x, layer)
+    T, dev = x.shape[0], x.device
+    r = {
+        "topk_idx": torch.empty((T, layer.K), dtype=torch.int32, device=dev),
+        "topk_w": torch.empty((T, layer.K), dtype=torch.float32, device=dev),
+        "offsets": torch.empty(layer.E + 1, dtype=torch.int32, device=dev),
+        "perm": torch.empty(max(1, T * layer.K), dtype=torch.int32, device=dev),
+        "shared_gate": torch.empty(max(1, T), dtype=torch.float32, device=dev),
+    }
+    r["logits"] = torch.empty((T, layer.E), dtype=torch.float32, device=dev) if want_logits else None
+    if ws is None:
+        ws = layer.workspace(T, dev)
+    rc = lib.moe_route(layer.desc, _ptr(x), T, _ptr(r["topk_idx"]), _ptr(r["topk_w"]), _ptr(r["offsets"]),
+                       _ptr(r["perm"]), _ptr(r["shared_gate"]), _ptr(r["logits"]), _ptr(ws), ws.numel(),
+                       _stream_handle(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_route")
+    return r

@@ -1,0 +1,80 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 codec, MFMA operand
+// types, wave-level reductions and the workspace descriptor.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (inputs finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float siluf_(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// 16-byte global load/store as four dwords.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// Device-side view of one layer and one call.
+struct LayerArgs {
+  int H, E, K, I, Is;
+  const bf16_t* router_w;       // [E, H]
+  const bf16_t* gate_up_w;      // [E, 2I, H]
+  const bf16_t* down_w;         // [E, H, I]
+  const bf16_t* sh_gate_w;      // [Is, H]
+  const bf16_t* sh_up_w;        // [Is, H]
+  const bf16_t* sh_down_w;      // [H, Is]
+  const bf16_t* sh_expert_gate; // [H]
+};
+
+// Carved workspace (all device pointers).
+struct Work {
+  int32_t* topk_idx;   // [T*K]
+  float* topk_w;       // [T*K]
+  float* gate_s;       // [T]
+  int32_t* blk_counts; // [nblk * E]  router-block histograms, then block bases
+  int32_t* offsets;    // [E + 1]
+  int32_t* tiles_gu;   // [E + 2]   prefix of gate_up tiles per group (group E = shared)
+  int32_t* tiles_dn;   // [E + 2]   prefix of down tiles per group
+  int32_t* perm;       // [T*K]
+  int32_t* slot_of;    // [T*K]
+  bf16_t* h;           // [T*K, I]
+  bf16_t* h_sh;        // [T, Is]
+  bf16_t* y;           // [T*K + T, H]  weighted expert outputs, routed slots then shared rows
+};
+
+}  // namespace moe

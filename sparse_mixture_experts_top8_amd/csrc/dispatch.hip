@@ -1,0 +1,108 @@
+// Dispatch of (token, k) pairs to contiguous per-expert segments: a counting
+// sort keyed by expert, stable in the pair id q = t*K + k.  The per-block
+// expert histograms come from the router kernel; here they are summed and
+// scanned into segment offsets and per-block bases, and each block then
+// scatters its pairs in order.  All integer work: the result is bit-exact.
+//
+// The pages say only that the router picks which experts receive a token
+// ("One Token Through Qwen3.6", section "The Router"; "Qwen3.6-35B-A3B —
+// Architecture Overview", section "MoE FFN: 256 Experts": only 8 of 256 fire
+// per token); grouping the pairs by expert is how this implementation lets
+// each expert run once as a dense GEMM over its rows.
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+// Inclusive prefix sum over the 256 threads of a block (4 wavefronts).
+__device__ int block_inclusive_scan(int v, int* wave_tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) wave_tot[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < wave; ++i) add += wave_tot[i];
+  __syncthreads();
+  return v + add;
+}
+
+// One workgroup: expert counts, segment offsets, per-block bases and the tile
+// prefix sums of both grouped GEMMs (group E is the shared expert, T rows).
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, Work w) {
+  __shared__ int wave_tot[4];
+  __shared__ int s_off[257];
+  const int e = threadIdx.x;
+  const int E = L.E, K = L.K;
+  const int nblk = router_blocks(T);
+  int cnt = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) cnt += w.blk_counts[(size_t)b * E + e];
+  const int incl = block_inclusive_scan(e < E ? cnt : 0, wave_tot);
+  const int off = incl - (e < E ? cnt : 0);
+  if (e < E) {
+    w.offsets[e] = off;
+    s_off[e] = off;
+    int run = off;
+    for (int b = 0; b < nblk; ++b) {
+      int c = w.blk_counts[(size_t)b * E + e];
+      w.blk_counts[(size_t)b * E + e] = run;
+      run += c;
+    }
+  }
+  if (e == 0) w.offsets[E] = T * K;
+
+  // Tiles per group: ceil(rows / BM) row tiles x (weight rows / BNW) column tiles.
+  int gu = 0, dn = 0;
+  if (e < E) {
+    int mt = (cnt + kGemmBM - 1) / kGemmBM;
+    gu = mt * (2 * L.I / kGemmBNW);
+    dn = mt * (L.H / kGemmBNW);
+  }
+  const int gu_incl = block_inclusive_scan(gu, wave_tot);
+  const int dn_incl = block_inclusive_scan(dn, wave_tot);
+  if (e < E) {
+    w.tiles_gu[e] = gu_incl - gu;
+    w.tiles_dn[e] = dn_incl - dn;
+  }
+  if (e == E - 1) {
+    const int mt = (T + kGemmBM - 1) / kGemmBM;
+    w.tiles_gu[E] = gu_incl;
+    w.tiles_dn[E] = dn_incl;
+    w.tiles_gu[E + 1] = gu_incl + mt * (2 * L.Is / kGemmBNW);
+    w.tiles_dn[E + 1] = dn_incl + mt * (L.H / kGemmBNW);
+  }
+}
+
+// Stable scatter of one router block's pairs (at most 32*K <= 256).
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(LayerArgs L, int T, Work w) {
+  __shared__ int keys[256];
+  const int E = L.E, K = L.K;
+  const int j = threadIdx.x;
+  const int q0 = blockIdx.x * kRouterTokens * K;
+  const int n = min(kRouterTokens * K, T * K - q0);
+  const int key = j < n ? w.topk_idx[q0 + j] : -1;
+  keys[j] = key;
+  __syncthreads();
+  if (j < n) {
+    int rank = 0;
+    for (int i = 0; i < j; ++i) rank += (keys[i] == key);
+    const int slot = w.blk_counts[(size_t)blockIdx.x * E + key] + rank;
+    w.perm[slot] = q0 + j;
+    w.slot_of[q0 + j] = slot;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s) {
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, L, T, w);
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(router_blocks(T)), dim3(256), 0, s, L, T, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

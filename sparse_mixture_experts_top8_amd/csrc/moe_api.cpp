@@ -1,0 +1,233 @@
+// C ABI of the MoE layer: argument checks, workspace carving and the launch
+// sequence.  Declared in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+using moe::bf16_t;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+constexpr int64_t kMaxTokens = int64_t(1) << 22;
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const moe_layer_t* L, int64_t T) {
+  if (!L) return fail(MOE_ERR_NULL, "layer descriptor is NULL");
+  const int64_t H = L->hidden, E = L->num_experts, K = L->top_k, I = L->expert_inner, Is = L->shared_inner;
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T = %lld is negative", (long long)T);
+  if (T > kMaxTokens) return fail(MOE_ERR_SHAPE, "T = %lld exceeds the supported maximum %lld", (long long)T, (long long)kMaxTokens);
+  if (H <= 0 || H % 256) return fail(MOE_ERR_SHAPE, "hidden = %lld must be a positive multiple of 256", (long long)H);
+  if (E < 1 || E > 256) return fail(MOE_ERR_SHAPE, "num_experts = %lld must be in [1, 256]", (long long)E);
+  if (K < 1 || K > 8 || K > E) return fail(MOE_ERR_SHAPE, "top_k = %lld must be in [1, min(8, num_experts)]", (long long)K);
+  if (I <= 0 || I % 64) return fail(MOE_ERR_SHAPE, "expert_inner = %lld must be a positive multiple of 64", (long long)I);
+  if (Is <= 0 || Is % 64) return fail(MOE_ERR_SHAPE, "shared_inner = %lld must be a positive multiple of 64", (long long)Is);
+  return MOE_OK;
+}
+
+struct Carve {
+  moe::Work w;
+  size_t bytes;
+};
+
+// Workspace layout, each region 256-byte aligned.  With base == nullptr only
+// the size is computed.
+Carve carve(const moe_layer_t* L, int64_t T, char* base) {
+  const size_t H = L->hidden, E = L->num_experts, K = L->top_k, I = L->expert_inner, Is = L->shared_inner;
+  const size_t t = (size_t)T, tk = t * K, nblk = (size_t)moe::router_blocks(T);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  Carve c{};
+  c.w.topk_idx = (int32_t*)take(tk * 4);
+  c.w.topk_w = (float*)take(tk * 4);
+  c.w.gate_s = (float*)take(t * 4);
+  c.w.blk_counts = (int32_t*)take(nblk * E * 4);
+  c.w.offsets = (int32_t*)take((E + 1) * 4);
+  c.w.tiles_gu = (int32_t*)take((E + 2) * 4);
+  c.w.tiles_dn = (int32_t*)take((E + 2) * 4);
+  c.w.perm = (int32_t*)take(tk * 4);
+  c.w.slot_of = (int32_t*)take(tk * 4);
+  c.w.h = (bf16_t*)take(tk * I * 2);
+  c.w.h_sh = (bf16_t*)take(t * Is * 2);
+  c.w.y = (bf16_t*)take((tk + t) * H * 2);
+  c.bytes = off;
+  return c;
+}
+
+moe::LayerArgs layer_args(const moe_layer_t* L) {
+  moe::LayerArgs a;
+  a.H = L->hidden;
+  a.E = L->num_experts;
+  a.K = L->top_k;
+  a.I = L->expert_inner;
+  a.Is = L->shared_inner;
+  a.router_w = (const bf16_t*)L->router_w;
+  a.gate_up_w = (const bf16_t*)L->gate_up_w;
+  a.down_w = (const bf16_t*)L->down_w;
+  a.sh_gate_w = (const bf16_t*)L->shared_gate_w;
+  a.sh_up_w = (const bf16_t*)L->shared_up_w;
+  a.sh_down_w = (const bf16_t*)L->shared_down_w;
+  a.sh_expert_gate = (const bf16_t*)L->shared_expert_gate_w;
+  return a;
+}
+
+int check_weights(const moe_layer_t* L) {
+  const void* p[7] = {L->router_w, L->gate_up_w, L->down_w, L->shared_gate_w,
+                      L->shared_up_w, L->shared_down_w, L->shared_expert_gate_w};
+  static const char* names[7] = {"router_w", "gate_up_w", "down_w", "shared_gate_w",
+                                 "shared_up_w", "shared_down_w", "shared_expert_gate_w"};
+  for (int i = 0; i < 7; ++i) {
+    if (!p[i]) return fail(MOE_ERR_NULL, "%s is NULL", names[i]);
+    if (!aligned16(p[i])) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  return MOE_OK;
+}
+
+// Per-device facts, looked up once: is it a gfx950, how many CUs.
+struct DeviceInfo {
+  std::once_flag once;
+  bool ok = false;
+  int cus = 0;
+  char arch[64] = {0};
+};
+DeviceInfo g_dev[64];
+
+int device_check(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "device index %d out of range", dev);
+  DeviceInfo& d = g_dev[dev];
+  std::call_once(d.once, [&] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      std::strncpy(d.arch, prop.gcnArchName, sizeof d.arch - 1);
+      d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      d.cus = prop.multiProcessorCount;
+    }
+  });
+  if (!d.ok) return fail(MOE_ERR_DEVICE, "device %d is '%s', not gfx950", dev, d.arch);
+  *cus = d.cus;
+  return MOE_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_layer_t* L, int64_t T) {
+  if (check_dims(L, T) != MOE_OK || T <= 0) return 0;
+  return carve(L, T, nullptr).bytes;
+}
+
+int moe_validate(const moe_layer_t* L, const void* x, int64_t T, const void* out, const void* ws,
+                 size_t ws_bytes) {
+  int rc = check_dims(L, T);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_weights(L)) != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x) return fail(MOE_ERR_NULL, "x is NULL");
+  if (!out) return fail(MOE_ERR_NULL, "out is NULL");
+  if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
+  if (!aligned16(x)) return fail(MOE_ERR_ALIGN, "x is not 16-byte aligned");
+  if (!aligned16(out)) return fail(MOE_ERR_ALIGN, "out is not 16-byte aligned");
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const size_t need = carve(L, T, nullptr).bytes;
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T = %lld", ws_bytes, need, (long long)T);
+  return MOE_OK;
+}
+
+int moe_route(const moe_layer_t* L, const void* x, int64_t T, int32_t* topk_idx, float* topk_w,
+              int32_t* offsets, int32_t* perm, float* shared_gate, float* logits, void* ws,
+              size_t ws_bytes, void* stream) {
+  int rc = check_dims(L, T);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_weights(L)) != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_idx || !topk_w || !offsets || !perm || !ws)
+    return fail(MOE_ERR_NULL, "x, topk_idx, topk_w, offsets, perm and workspace are required");
+  const void* ptrs[8] = {x, topk_idx, topk_w, offsets, perm, ws, shared_gate, logits};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(MOE_ERR_ALIGN, "a pointer argument is not 16-byte aligned");
+  Carve c = carve(L, T, (char*)ws);
+  if (ws_bytes < c.bytes)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T = %lld", ws_bytes, c.bytes, (long long)T);
+  int cus = 0;
+  if ((rc = device_check(&cus)) != MOE_OK) return rc;
+  moe::Work w = c.w;
+  w.topk_idx = topk_idx;
+  w.topk_w = topk_w;
+  w.offsets = offsets;
+  w.perm = perm;
+  if (shared_gate) w.gate_s = shared_gate;
+  const moe::LayerArgs a = layer_args(L);
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, (int)T, w, logits, s), "router")) != MOE_OK) return rc;
+  return launch_status(moe::launch_dispatch(a, (int)T, w, s), "dispatch");
+}
+
+int moe_forward(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = moe_validate(L, x, T, out, ws, ws_bytes);
+  if (rc != MOE_OK || T == 0) return rc;
+  int cus = 0;
+  if ((rc = device_check(&cus)) != MOE_OK) return rc;
+  const moe::Work w = carve(L, T, (char*)ws).w;
+  const moe::LayerArgs a = layer_args(L);
+  hipStream_t s = (hipStream_t)stream;
+  const int t = (int)T;
+  if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, t, w, nullptr, s), "router")) != MOE_OK) return rc;
+  if ((rc = launch_status(moe::launch_dispatch(a, t, w, s), "dispatch")) != MOE_OK) return rc;
+  if ((rc = launch_status(moe::launch_gate_up(a, (const bf16_t*)x, t, w, cus, s), "gate_up")) != MOE_OK) return rc;
+  if ((rc = launch_status(moe::launch_down(a, t, w, cus, s), "down")) != MOE_OK) return rc;
+  return launch_status(moe::launch_combine(a, t, w, (bf16_t*)out, s), "combine");
+}
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "unsupported or invalid dimensions";
+    case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_DEVICE: return "current device is not a gfx950";
+    case MOE_ERR_LAUNCH: return "a HIP call failed";
+    default: return "unknown status code";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports what include/moe.h
+declares, and its host-side checks return the documented codes before any
+HIP call (fake, never-dereferenced pointers are enough for that)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_mixture_experts_top8_amd as moe
+from sparse_mixture_experts_top8_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced by the checks
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def _layer(H=2048, E=256, K=8, I=512, Is=512, ptr=FAKE):
+    return _lib.MoeLayerT(H, E, K, I, Is, *([ptr] * 7))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(_lib.lib, name)
+
+
+def test_strerror_covers_codes():
+    for code in range(7):
+        assert _lib.strerror(code) and _lib.strerror(code) != "unknown status code"
+    assert _lib.strerror(99) == "unknown status code"
+
+
+def test_workspace_bytes():
+    L = _layer()
+    assert _lib.lib.moe_workspace_bytes(L, 0) == 0
+    assert _lib.lib.moe_workspace_bytes(L, -1) == 0
+    sizes = [_lib.lib.moe_workspace_bytes(L, T) for T in (1, 64, 4096, 16384)]
+    assert all(a < b for a, b in zip(sizes, sizes[1:]))
+    # At least the per-slot bf16 expert outputs and intermediates must fit.
+    T = 4096
+    assert sizes[2] >= (T * 8 + T) * 2048 * 2 + T * 8 * 512 * 2
+    assert _lib.lib.moe_workspace_bytes(_layer(H=100), 4) == 0
+
+
+def _validate(L, x=FAKE, T=4, out=FAKE, ws=FAKE, nbytes=None):
+    if nbytes is None:
+        nbytes = _lib.lib.moe_workspace_bytes(L, max(T, 1))
+    return _lib.lib.moe_validate(L, x, T, out, ws, nbytes)
+
+
+def test_validate_accepts_good_arguments():
+    assert _validate(_layer()) == _lib.MOE_OK
+    assert _validate(_layer(H=256, E=16, K=4, I=64, Is=64)) == _lib.MOE_OK
+    assert _validate(_layer(), x=None, out=None, ws=None, T=0, nbytes=0) == _lib.MOE_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=2000), _lib.MOE_ERR_SHAPE), (dict(H=0), _lib.MOE_ERR_SHAPE),
+    (dict(E=0), _lib.MOE_ERR_SHAPE), (dict(E=257), _lib.MOE_ERR_SHAPE),
+    (dict(K=0), _lib.MOE_ERR_SHAPE), (dict(K=9), _lib.MOE_ERR_SHAPE),
+    (dict(E=4, K=5), _lib.MOE_ERR_SHAPE), (dict(I=500), _lib.MOE_ERR_SHAPE),
+    (dict(Is=0), _lib.MOE_ERR_SHAPE), (dict(ptr=FAKE + 8), _lib.MOE_ERR_ALIGN),
+])
+def test_validate_rejects_layer(kw, code):
+    assert _validate(_layer(**kw)) == code
+    assert _lib.last_error()
+
+
+def test_validate_rejects_call_arguments():
+    L = _layer()
+    assert _validate(L, T=-1) == _lib.MOE_ERR_SHAPE
+    assert _validate(L, T=(1 << 22) + 1, nbytes=1 << 62) == _lib.MOE_ERR_SHAPE
+    assert _validate(L, x=None) == _lib.MOE_ERR_NULL
+    assert _validate(L, out=None) == _lib.MOE_ERR_NULL
+    assert _validate(L, ws=None) == _lib.MOE_ERR_NULL
+    assert _validate(L, x=FAKE + 2) == _lib.MOE_ERR_ALIGN
+    assert _validate(L, out=FAKE + 4) == _lib.MOE_ERR_ALIGN
+    assert _validate(L, ws=FAKE + 8) == _lib.MOE_ERR_ALIGN
+    need = _lib.lib.moe_workspace_bytes(L, 4)
+    assert _validate(L, nbytes=need - 1) == _lib.MOE_ERR_WORKSPACE
+    assert "needed" in _lib.last_error()
+    nulled = _layer()
+    nulled.down_w = None
+    assert _validate(nulled) == _lib.MOE_ERR_NULL
+    assert "down_w" in _lib.last_error()
+    assert _lib.lib.moe_validate(None, FAKE, 4, FAKE, FAKE, 1 << 30) == _lib.MOE_ERR_NULL
+
+
+def test_entry_points_fail_before_any_hip_call():
+    L = _layer()
+    need = _lib.lib.moe_workspace_bytes(L, 4)
+    assert _lib.lib.moe_forward(L, FAKE, 4, FAKE, FAKE, need - 1, None) == _lib.MOE_ERR_WORKSPACE
+    assert _lib.lib.moe_forward(L, FAKE, -3, FAKE, FAKE, need, None) == _lib.MOE_ERR_SHAPE
+    assert _lib.lib.moe_forward(L, None, 0, None, None, 0, None) == _lib.MOE_OK
+    assert _lib.lib.moe_route(L, FAKE, 4, None, FAKE, FAKE, FAKE, None, None, FAKE, need, None) == _lib.MOE_ERR_NULL
+    assert _lib.lib.moe_route(L, FAKE, 4, FAKE + 4, FAKE, FAKE, FAKE, None, None, FAKE, need, None) == _lib.MOE_ERR_ALIGN
+    assert _lib.lib.moe_route(L, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, need - 1, None) == _lib.MOE_ERR_WORKSPACE
+    assert _lib.lib.moe_route(L, None, 0, None, None, None, None, None, None, None, 0, None) == _lib.MOE_OK
+
+
+def test_python_wrappers_check_inputs():
+    import torch
+    layer_bits_shape = dict(H=256, E=16, K=4, I=64, Is=64)
+    params = {n: torch.zeros(4, dtype=torch.bfloat16) for n in moe.PARAM_NAMES}
+    layer = moe.MoeLayer(params=params, **layer_bits_shape)
+    with pytest.raises(ValueError):
+        moe.forward(torch.zeros(3, 255, dtype=torch.bfloat16), layer)
+    with pytest.raises(ValueError):
+        moe.forward(torch.zeros(3, 256, dtype=torch.float32), layer)
+    with pytest.raises(ValueError):
+        moe.MoeLayer(params={n: torch.zeros(4) for n in moe.PARAM_NAMES}, **layer_bits_shape)

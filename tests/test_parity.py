@@ -1,0 +1,259 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar (per output element): expert indices bit-exact except tokens the oracle
+flags as router ties (two of ranks 0..K closer than 1e-6 in float64 logits);
+for those, every selected expert must score within 1e-6 of the K-th best.
+Offsets and the permutation are bit-exact against the oracle's counting sort
+of the GPU's indices.  The shared gate within 1e-6.
+Router logits within the fp32 rounding bound of their dot products; weights
+within 1e-6 of the renormalised softmax of those logits (a logit of size 50
+has an fp32 spacing of 4e-6, so weights against the float64 oracle can only
+be held to that scale).
+Output max-abs <= 2e-2 and relative L2 <= 1e-2 against the float64 oracle
+evaluated with the GPU's expert choice (identical to the oracle's own for
+unflagged tokens).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from oracle import moe_oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 1e-2
+W_TOL = 1e-6
+# Roundings on the longest path to one router logit: a 32-term MFMA dot
+# product, 8 accumulator steps per 256-element chunk, 8 chunk totals (H=2048).
+LOGIT_CHAIN = 48
+
+
+def _moe():
+    import sparse_mixture_experts_top8_amd as moe
+    return moe
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def check_routing(xb, bits, dims, r, tag):
+    K, E = dims.K, dims.E
+    T = xb.shape[0]
+    R = O.route(xb, bits, K)
+    gi = _np(r["topk_idx"])
+    oi = R["topk_idx"]
+    tie = R["tie"]
+    diff = (gi != oi).any(axis=1)
+    assert not (diff & ~tie).any(), f"{tag}: index mismatch on unflagged tokens {np.nonzero(diff & ~tie)[0][:10]}"
+    # Every chosen expert is a valid choice: distinct, and within the tie gap of the K-th best.
+    assert all(len(set(row)) == K for row in gi)
+    kth = np.sort(R["logits"], axis=1)[:, ::-1][:, K - 1]
+    chosen = np.take_along_axis(R["logits"], gi.astype(np.int64), axis=1)
+    assert np.all(chosen >= kth[:, None] - O.TIE_GAP), tag
+    gw = _np(r["topk_w"]).astype(np.float64)
+    if r.get("logits") is not None:
+        # Logits: fp32 accumulation of bf16 products; the rounding bound of a
+        # dot product whose longest chain of roundings is LOGIT_CHAIN steps is
+        # LOGIT_CHAIN * 2^-24 * sum_h |x_h w_h|.
+        gl = _np(r["logits"]).astype(np.float64)
+        S = np.abs(O.bf16_to_f64(xb)) @ np.abs(O.bf16_to_f64(bits["gate.weight"])).T
+        bound = LOGIT_CHAIN * 2.0 ** -24 * S
+        err_l = np.abs(gl - R["logits"])
+        assert np.all(err_l <= bound), f"{tag}: logit error {err_l.max():.3e}"
+        # Softmax and renormalisation of the GPU's own logits: within 1e-6.
+        np.testing.assert_allclose(gw, O.renormalised_weights(gl, gi), rtol=0, atol=W_TOL)
+        _say(f"{tag}: max logit error {err_l.max():.3e} (max bound {bound.max():.3e}), "
+             f"weight error vs oracle {np.abs(gw - O.renormalised_weights(R['logits'], gi)).max():.3e}")
+    else:
+        np.testing.assert_allclose(gw, O.renormalised_weights(R["logits"], gi), rtol=0, atol=W_TOL)
+    d = O.counting_sort(gi, E)
+    assert np.array_equal(_np(r["offsets"]), d["offsets"]), tag
+    assert np.array_equal(_np(r["perm"])[:T * K], d["perm"]), tag
+    np.testing.assert_allclose(_np(r["shared_gate"])[:T], R["shared_gate"], rtol=0, atol=W_TOL)
+    _say(f"{tag}: routing ok, T={T}, flagged ties {int(tie.sum())}, index diffs on flagged {int(diff.sum())}")
+    return gi
+
+
+def check_output(xb, bits, dims, gi, out_rows, rows, tag):
+    ref = O.forward_with_routing(xb[rows], bits, gi[rows])
+    got = out_rows.astype(np.float64)
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    rms = np.sqrt(np.mean(ref ** 2))
+    _say(f"{tag}: rows {len(rows)} max-abs {err.max():.3e} rel-L2 {rel:.3e} (ref rms {rms:.3e})")
+    assert err.max() <= MAX_ABS, tag
+    assert rel <= REL_L2, tag
+
+
+def run_layer(layer, xb, want_logits=False):
+    moe = _moe()
+    x = moe.bits_to_device(xb, "cuda")
+    r = moe.route(x, layer, want_logits=want_logits)
+    out = moe.forward(x, layer)
+    torch.cuda.synchronize()
+    return r, out
+
+
+# ---------------------------------------------------------------------------
+# Toy shape (H=256, E=16, K=4, I=Is=64): whole-output comparison.
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def toy():
+    moe = _moe()
+    d = mi.TOY
+    bits = mi.workload_layer(mi.WORKLOADS["toy"])
+    return d, bits, moe.MoeLayer.from_bf16_bits(bits, d.H, d.E, d.K, d.I, d.Is, "cuda")
+
+
+@pytest.mark.parametrize("T", [8, 1, 2, 31, 32, 33, 63, 64, 65, 127, 129, 300, 1000])
+def test_toy_parity(toy, T):
+    d, bits, layer = toy
+    _say(f"case toy T={T}")
+    xb = mi.workload_x(mi.WORKLOADS["toy"]) if T == 8 else mi.make_x(d, T, 1000 + T)
+    r, out = run_layer(layer, xb, want_logits=True)
+    gi = check_routing(xb, bits, d, r, f"toy T={T}")
+    check_output(xb, bits, d, gi, _np(out.float()), np.arange(T), f"toy T={T}")
+
+
+def test_toy_small_inputs_and_ties(toy):
+    d, bits, layer = toy
+    _say("case toy x~N(0,0.02)")
+    xb = mi.make_x(d, 200, 77, std=0.02)
+    r, out = run_layer(layer, xb)
+    gi = check_routing(xb, bits, d, r, "toy small x")
+    check_output(xb, bits, d, gi, _np(out.float()), np.arange(200), "toy small x")
+
+
+def test_toy_zero_input_all_ties(toy):
+    d, bits, layer = toy
+    _say("case toy x=0")
+    xb = np.zeros((40, d.H), np.uint16)
+    r, out = run_layer(layer, xb)
+    assert np.all(_np(r["topk_idx"]) == np.arange(d.K))
+    np.testing.assert_allclose(_np(r["topk_w"]), 1.0 / d.K, rtol=0, atol=1e-7)
+    assert np.all(_np(out.float()) == 0.0)
+
+
+def test_toy_other_k_and_e():
+    moe = _moe()
+    for (E, K) in [(8, 8), (16, 1), (32, 8), (256, 8)]:
+        d = mi.Dims(H=256, E=E, K=K, I=64, Is=128)
+        _say(f"case toy E={E} K={K} Is=128")
+        bits = mi.make_layer(d, 500 + E + K)
+        layer = moe.MoeLayer.from_bf16_bits(bits, d.H, d.E, d.K, d.I, d.Is, "cuda")
+        xb = mi.make_x(d, 70, 600 + E)
+        r, out = run_layer(layer, xb)
+        gi = check_routing(xb, bits, d, r, f"E={E} K={K}")
+        check_output(xb, bits, d, gi, _np(out.float()), np.arange(70), f"E={E} K={K}")
+
+
+def test_toy_empty_and_determinism(toy):
+    moe = _moe()
+    d, bits, layer = toy
+    _say("case toy T=0 / determinism / guard bands / permutation")
+    x0 = torch.empty((0, d.H), dtype=torch.bfloat16, device="cuda")
+    assert moe.forward(x0, layer).shape == (0, d.H)
+    xb = mi.make_x(d, 257, 4242)
+    x = moe.bits_to_device(xb, "cuda")
+    # Guard bands around out and the workspace must stay untouched.
+    T = xb.shape[0]
+    big = torch.full((T * d.H + 2 * 4096,), 12345, dtype=torch.int16, device="cuda")
+    out = big[4096:4096 + T * d.H].view(torch.bfloat16).view(T, d.H)
+    need = layer.workspace_bytes(T)
+    ws_big = torch.full((need + 2 * 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = ws_big[4096:4096 + need]
+    moe.forward(x, layer, out=out, ws=ws)
+    a = out.clone()
+    moe.forward(x, layer, out=out, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), out.view(torch.int16)), "not bitwise reproducible"
+    assert torch.all(big[:4096] == 12345) and torch.all(big[4096 + T * d.H:] == 12345)
+    assert torch.all(ws_big[:4096] == 0xA5) and torch.all(ws_big[4096 + need:] == 0xA5)
+    # Permuting tokens permutes output rows bit for bit.
+    p = np.random.default_rng(1).permutation(T)
+    outp = moe.forward(moe.bits_to_device(xb[p], "cuda"), layer)
+    torch.cuda.synchronize()
+    assert torch.equal(outp.view(torch.int16).cpu(), a.view(torch.int16).cpu()[p])
+
+
+# ---------------------------------------------------------------------------
+# Full shape (H=2048, E=256, K=8, I=Is=512).
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def full():
+    moe = _moe()
+    d = mi.FULL
+    _say("generating the full-shape layer")
+    bits = mi.workload_layer(mi.WORKLOADS["decode1"])
+    layer = moe.MoeLayer.from_bf16_bits(bits, d.H, d.E, d.K, d.I, d.Is, "cuda")
+    zb = dict(bits)
+    zb["gate.weight"] = mi.make_router(d, mi.WORKLOADS["zipf16384"].layer_seed, mi.zipf_router_gain())
+    zparams = dict(layer.params)
+    zparams["gate.weight"] = moe.bits_to_device(zb["gate.weight"], "cuda")
+    zlayer = moe.MoeLayer(d.H, d.E, d.K, d.I, d.Is, zparams)
+    return d, bits, layer, zb, zlayer
+
+
+def _sample_rows(T, gi, hot_expert=None, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(8, T))) | set(range(max(0, T - 8), T))
+    rows |= set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    if hot_expert is not None:
+        hot = np.nonzero((gi == hot_expert).any(axis=1))[0]
+        rows |= set(hot[:8].tolist()) | set(hot[-8:].tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode64", "prefill4096", "zipf16384"])
+def test_full_workloads(full, name):
+    d, bits, layer, zb, zlayer = full
+    wl = mi.WORKLOADS[name]
+    _say(f"case full {name} T={wl.T}")
+    lb, ly = (zb, zlayer) if wl.skewed_router else (bits, layer)
+    xb = mi.workload_x(wl)
+    r, out = run_layer(ly, xb, want_logits=True)
+    gi = check_routing(xb, lb, d, r, name)
+    counts = np.bincount(gi.reshape(-1), minlength=d.E)
+    _say(f"{name}: experts touched {int((counts > 0).sum())}, max load {counts.max()}, "
+         f"mean {counts.mean():.1f}")
+    if wl.skewed_router:
+        assert counts.max() >= 10 * counts.mean()
+    rows = np.arange(wl.T) if wl.T <= 64 else _sample_rows(wl.T, gi, int(np.argmax(counts)))
+    check_output(xb, lb, d, gi, _np(out.float())[rows], rows, name)
+
+
+def test_full_decode_small_inputs(full):
+    d, bits, layer, _, _ = full
+    _say("case full decode x~N(0,0.02)")
+    for T in (1, 5):
+        xb = mi.make_x(d, T, 9000 + T, std=0.02)
+        r, out = run_layer(layer, xb)
+        gi = check_routing(xb, bits, d, r, f"decode small x T={T}")
+        check_output(xb, bits, d, gi, _np(out.float()), np.arange(T), f"decode small x T={T}")
+
+
+def test_full_forced_routing_one_hot_segment(full):
+    # Identical tokens: all pick the same 8 experts, so 8 segments hold every
+    # token and 248 experts are empty; all output rows must be identical.
+    moe = _moe()
+    d, bits, layer, _, _ = full
+    _say("case full forced routing T=777")
+    xb = np.repeat(mi.make_x(d, 1, 31337), 777, axis=0)
+    r, out = run_layer(layer, xb)
+    gi = check_routing(xb, bits, d, r, "forced")
+    assert len(np.unique(gi, axis=0)) == 1
+    o = out.view(torch.int16)
+    assert torch.all(o == o[0:1]).item()
+    check_output(xb[:1], bits, d, gi[:1], _np(out.float())[:1], np.arange(1), "forced")
+    del moe
