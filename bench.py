@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer (256 experts, top-8, gated shared expert) on one MI355X.
+
+A step is one moe_forward call (router, top-K, dispatch, both expert GEMMs,
+shared expert, combine) over one batch of seeded synthetic tokens, with the
+inputs already resident in HBM.  Steps rotate over several independently drawn
+layers so that weights are not served from the 256 MB Infinity Cache across
+steps (8 layers at T = 1, 2 otherwise).
+
+    python bench.py                       # 1-token decode, the default workload
+    python bench.py --workload prefill4096 --steps 50 --warmup 5
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+DEFAULTS = {  # workload -> (steps, warmup, layers rotated)
+    "decode1": (2000, 100, 8),
+    "decode64": (200, 20, 2),
+    "prefill4096": (50, 5, 2),
+    "zipf16384": (20, 3, 2),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode1", choices=sorted(DEFAULTS))
+    ap.add_argument("--layers", type=int, default=None, help="weight sets rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: 5 copies of {n} bytes ({n // 1024} KiB read and written per copy)")
+    print(json.dumps({"copy_probe_bytes": n}))
+
+
+def device_layer(moe, mi, wl, l, base_bits):
+    """Layer l of the rotation: layer 0 from the seeded CPU generator, the others
+    drawn on the device (torch generator seeded layer_seed*100 + l)."""
+    import torch
+    d = wl.dims
+    if l == 0:
+        bits = dict(base_bits)
+        return moe.MoeLayer.from_bf16_bits(bits, d.H, d.E, d.K, d.I, d.Is, "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.layer_seed * 100 + l)
+    params = {}
+    for name, shape in d.shapes().items():
+        t = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).mul_(mi.WEIGHT_STD)
+        if name == "gate.weight" and wl.skewed_router:
+            t.mul_(torch.tensor(mi.zipf_router_gain(), device="cuda", dtype=torch.float32).view(-1, 1))
+        params[name] = t.to(torch.bfloat16).contiguous()
+        del t
+    return moe.MoeLayer(d.H, d.E, d.K, d.I, d.Is, params)
+
+
+def device_x(moe, mi, wl, l):
+    import torch
+    if l == 0:
+        return moe.bits_to_device(mi.workload_x(wl), "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.x_seed * 100 + l)
+    return (torch.randn((wl.T, wl.dims.H), generator=g, device="cuda") * wl.x_std).to(torch.bfloat16)
+
+
+def phase_work(d, T, U, phase):
+    """Algorithmic (bytes, flops) of one launch of a phase.  Bytes count each
+    touched expert's weights once, plus the inputs/outputs of the layer that
+    the phase must read or write; intermediates are excluded."""
+    H, E, K, I, Is = d.H, d.E, d.K, d.I, d.Is
+    if phase == "router":
+        return 2 * (E * H + T * H + H), 2 * T * H * (E + 1)
+    if phase == "dispatch":
+        return 0, 0
+    if phase == "gate_up":
+        return 2 * (U * 2 * I * H + 2 * Is * H + T * H), 2 * T * K * H * 2 * I + 2 * T * H * 2 * Is
+    if phase == "down":
+        return 2 * (U * H * I + H * Is), 2 * T * K * I * H + 2 * T * Is * H
+    if phase == "combine":
+        return 2 * T * H, 0
+    raise KeyError(phase)
+
+
+def step_work(d, T, U):
+    """Algorithmic bytes and flops of one whole layer call."""
+    per_expert = 2 * 3 * d.H * d.I
+    nbytes = U * per_expert + 2 * 3 * d.H * d.Is + 2 * d.E * d.H + 2 * d.H + 2 * 2 * T * d.H
+    flops = T * 2 * (d.K * 3 * d.H * d.I + 3 * d.H * d.Is + d.E * d.H + d.H)
+    return nbytes, flops
+
+
+def cpu_baseline(mi, wl, bits, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as O
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    d = wl.dims
+    if wl.T == 1:
+        xs = mi.make_x(d, 4096, wl.x_seed + 7000, wl.x_std)
+        n, t0 = 0, time.perf_counter()
+        while n < 3 or (time.perf_counter() - t0 < budget_s and n < xs.shape[0]):
+            O.forward(xs[n:n + 1], bits, d.K)
+            n += 1
+        el = time.perf_counter() - t0
+        sample = f"{n} single-token calls (fresh x each), oracle.forward, float64"
+        return {"value": n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": sample, "seconds": round(el, 2)}
+    x = mi.workload_x(wl)
+    n = 8
+    while True:
+        t0 = time.perf_counter()
+        O.forward(x[:n], bits, d.K)
+        el = time.perf_counter() - t0
+        if el > budget_s / 3 or n >= wl.T:
+            break
+        n = min(wl.T, n * 4)
+    sample = f"first {n} tokens of the {wl.T}-token batch in one oracle.forward call, float64"
+    return {"value": n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is measured on a "
+              f"single MI355X and no multi-GPU path exists", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        return copy_probe()
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import sparse_mixture_experts_top8_amd as moe
+
+    wl = mi.WORKLOADS[args.workload]
+    d = wl.dims
+    steps, warmup, nlayers = DEFAULTS[args.workload]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+    nlayers = args.layers if args.layers is not None else nlayers
+    T = wl.T
+
+    prop = torch.cuda.get_device_properties(0)
+    log(f"device {prop.name} ({getattr(prop, 'gcnArchName', '?')}), {prop.multi_processor_count} CUs")
+    log(f"workload {wl.name}: T={T}, {nlayers} layers rotated, steps {steps}, warmup {warmup}")
+    t0 = time.time()
+    base_bits = mi.workload_layer(wl)
+    layers = [device_layer(moe, mi, wl, l, base_bits) for l in range(nlayers)]
+    xs = [device_x(moe, mi, wl, l) for l in range(nlayers)]
+    outs = [torch.empty_like(x) for x in xs]
+    ws = layers[0].workspace(T)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    # Touched experts per layer (for the byte model).
+    U = []
+    for l in range(nlayers):
+        r = moe.route(xs[l], layers[l], ws=ws)
+        U.append(int((torch.bincount(r["topk_idx"].view(-1).long(), minlength=d.E) > 0).sum()))
+    U_mean = float(np.mean(U))
+
+    for i in range(warmup):
+        l = i % nlayers
+        moe.forward(xs[l], layers[l], out=outs[l], ws=ws)
+    torch.cuda.synchronize()
+
+    # Timed region: steps back to back on the current stream; each step also
+    # records six events at its phase boundaries (on that same stream).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for e6 in ev:
+        for e in e6:
+            e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        l = i % nlayers
+        moe.forward_traced(xs[l], layers[l], outs[l], ws, ev[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / steps
+    phase_ms = {p: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
+                for j, p in enumerate(moe.PHASES)}
+    log("phase ms: " + ", ".join(f"{k} {v * 1e3:.1f}us" for k, v in phase_ms.items()))
+
+    # Untraced loop for comparison (event overhead).
+    torch.cuda.synchronize()
+    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s2.record()
+    for i in range(steps):
+        l = i % nlayers
+        moe.forward(xs[l], layers[l], out=outs[l], ws=ws)
+    e2.record()
+    torch.cuda.synchronize()
+    plain_ms_per_step = s2.elapsed_time(e2) / steps
+
+    step_bytes, step_flops = step_work(d, T, U_mean)
+    dom = max(phase_ms, key=phase_ms.get)
+    dbytes, dflops = phase_work(d, T, U_mean, dom)   # U: routed experts; shared added inside
+    dsec = phase_ms[dom] * 1e-3
+    mfma_bound = wl.name == "zipf16384"
+    if mfma_bound:
+        ach = dflops / dsec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        ach = dbytes / dsec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"kernel": dom, "kernel_us": round(phase_ms[dom] * 1e3, 2),
+                 "alg_bytes_per_launch": int(dbytes), "alg_flops_per_launch": int(dflops), "traffic": None})
+
+    sec = ms_per_step * 1e-3
+    layer_stats = {
+        "alg_bytes": int(step_bytes), "alg_flops": int(step_flops), "experts_touched": U_mean,
+        "hbm_frac": round(step_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(step_flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "attainable_frac": round(min(step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                                     step_bytes / (HBM_PEAK_GBS * 1e9)) / sec, 4),
+        "phase_us": {k: round(v * 1e3, 2) for k, v in phase_ms.items()},
+        "untraced_ms_per_step": round(plain_ms_per_step, 5),
+    }
+
+    result = {
+        "metric": "MoE-layer tokens/s + % HBM BW peak (decode) / % bf16 MFMA peak (prefill)",
+        "value": round(T / sec, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.note}; H={d.H} E={d.E} K={d.K} I={d.I} Is={d.Is} T={T}",
+                   "tokens_per_step": T, "layers_rotated": nlayers, "weights": "seeded N(0,0.02) bf16",
+                   "device": prop.name, "cus": prop.multi_processor_count},
+        "roofline": roof,
+        "layer": layer_stats,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(mi, wl, base_bits, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

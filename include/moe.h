@@ -112,6 +112,17 @@ int moe_route(const moe_layer_t *L, const void *x, int64_t T,
 int moe_forward(const moe_layer_t *L, const void *x, int64_t T, void *out,
                 void *ws, size_t ws_bytes, void *stream);
 
+/* moe_forward that also records caller-created HIP events (hipEvent_t) on
+ * `stream` at its phase boundaries, for timing the kernels:
+ *   events[0] before the router, [1] after the router (top-K, weights, shared
+ *   gate), [2] after dispatch (counting sort), [3] after the gate_up GEMM,
+ *   [4] after the down GEMM, [5] after the combine.
+ * A path that fuses phases records the boundaries it does not separate back
+ * to back.  events == NULL is exactly moe_forward.  Same arguments, errors
+ * and results as moe_forward. */
+int moe_forward_traced(const moe_layer_t *L, const void *x, int64_t T, void *out,
+                       void *ws, size_t ws_bytes, void *stream, void *const *events);
+
 /* Static text for a status code. */
 const char *moe_strerror(int code);
 

@@ -103,6 +103,22 @@ def forward(x: torch.Tensor, layer: MoeLayer, out: torch.Tensor | None = None,
     return out
 
 
+PHASES = ("router", "dispatch", "gate_up", "down", "combine")
+
+
+def forward_traced(x: torch.Tensor, layer: MoeLayer, out: torch.Tensor, ws: torch.Tensor,
+                   events, stream=None) -> torch.Tensor:
+    """forward() recording six timing events (torch.cuda.Event, already created)
+    at the phase boundaries listed in PHASES."""
+    import ctypes
+    arr = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
+    rc = lib.moe_forward_traced(layer.desc, _ptr(x), x.shape[0], _ptr(out), _ptr(ws), ws.numel(),
+                                _stream_handle(stream), arr)
+    if rc != 0:
+        raise MoeError(rc, "moe_forward_traced")
+    return out
+
+
 def route(x: torch.Tensor, layer: MoeLayer, ws: torch.Tensor | None = None, stream=None,
           want_logits: bool = False) -> dict:
     """Routing and dispatch only; returns device tensors."""

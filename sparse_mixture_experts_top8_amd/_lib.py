@@ -22,7 +22,7 @@ MOE_ERR_LAUNCH = 6
 
 # Exported entry points, as include/moe.h declares them.
 EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_forward",
-           "moe_strerror", "moe_last_error")
+           "moe_forward_traced", "moe_strerror", "moe_last_error")
 
 
 class MoeLayerT(ctypes.Structure):
@@ -51,7 +51,7 @@ class MoeError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                          f"or python -m sparse_mixture_experts_top8_amd.build")
+                          f"or python sparse_mixture_experts_top8_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     L = ctypes.POINTER(MoeLayerT)
@@ -63,6 +63,8 @@ def _load():
     lib.moe_route.restype = ctypes.c_int
     lib.moe_forward.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_traced.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P, P]
+    lib.moe_forward_traced.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
     lib.moe_strerror.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []

@@ -2,7 +2,7 @@
 
 Every call compiles from source with hipcc (cross-compiles without a GPU):
 
-    python -m sparse_mixture_experts_top8_amd.build
+    python sparse_mixture_experts_top8_amd/build.py
 """
 from __future__ import annotations
 

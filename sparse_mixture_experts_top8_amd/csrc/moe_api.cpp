@@ -198,8 +198,8 @@ int moe_route(const moe_layer_t* L, const void* x, int64_t T, int32_t* topk_idx,
   return launch_status(moe::launch_dispatch(a, (int)T, w, s), "dispatch");
 }
 
-int moe_forward(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws, size_t ws_bytes,
-                void* stream) {
+int moe_forward_traced(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws,
+                       size_t ws_bytes, void* stream, void* const* events) {
   int rc = moe_validate(L, x, T, out, ws, ws_bytes);
   if (rc != MOE_OK || T == 0) return rc;
   int cus = 0;
@@ -208,11 +208,26 @@ int moe_forward(const moe_layer_t* L, const void* x, int64_t T, void* out, void*
   const moe::LayerArgs a = layer_args(L);
   hipStream_t s = (hipStream_t)stream;
   const int t = (int)T;
+  auto mark = [&](int i) -> int {
+    if (!events) return MOE_OK;
+    return launch_status(hipEventRecord((hipEvent_t)events[i], s), "hipEventRecord");
+  };
+  if ((rc = mark(0)) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, t, w, nullptr, s), "router")) != MOE_OK) return rc;
+  if ((rc = mark(1)) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_dispatch(a, t, w, s), "dispatch")) != MOE_OK) return rc;
+  if ((rc = mark(2)) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_gate_up(a, (const bf16_t*)x, t, w, cus, s), "gate_up")) != MOE_OK) return rc;
+  if ((rc = mark(3)) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_down(a, t, w, cus, s), "down")) != MOE_OK) return rc;
-  return launch_status(moe::launch_combine(a, t, w, (bf16_t*)out, s), "combine");
+  if ((rc = mark(4)) != MOE_OK) return rc;
+  if ((rc = launch_status(moe::launch_combine(a, t, w, (bf16_t*)out, s), "combine")) != MOE_OK) return rc;
+  return mark(5);
+}
+
+int moe_forward(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws, size_t ws_bytes,
+                void* stream) {
+  return moe_forward_traced(L, x, T, out, ws, ws_bytes, stream, nullptr);
 }
 
 const char* moe_strerror(int code) {
