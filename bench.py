@@ -197,40 +197,44 @@ def main():
         moe.forward(xs[l], layers[l], out=outs[l], ws=ws)
     torch.cuda.synchronize()
 
-    # Timed region: steps back to back on the current stream; each step also
-    # records six events at its phase boundaries (on that same stream).
+    # Timed region: K steps back to back on the current stream, bracketed by
+    # events on that stream.
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        l = i % nlayers
+        moe.forward(xs[l], layers[l], out=outs[l], ws=ws)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+
+    # Kernel attribution: the same steps again, each recording six events at
+    # its phase boundaries on the same stream (the fused decode path records
+    # its single kernel between events 0 and 1).
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     for e6 in ev:
         for e in e6:
             e.record()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
     for i in range(steps):
         l = i % nlayers
         moe.forward_traced(xs[l], layers[l], outs[l], ws, ev[i])
-    end.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / steps
     phase_ms = {p: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
                 for j, p in enumerate(moe.PHASES)}
-    log("phase ms: " + ", ".join(f"{k} {v * 1e3:.1f}us" for k, v in phase_ms.items()))
-
-    # Untraced loop for comparison (event overhead).
-    torch.cuda.synchronize()
-    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s2.record()
-    for i in range(steps):
-        l = i % nlayers
-        moe.forward(xs[l], layers[l], out=outs[l], ws=ws)
-    e2.record()
-    torch.cuda.synchronize()
-    plain_ms_per_step = s2.elapsed_time(e2) / steps
+    fused = T <= 64 and d.H <= 2048 and d.I <= 512 and d.Is <= 512
+    if fused:
+        phase_ms = {"decode_fused": phase_ms["router"]}
+    log("phase us: " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in phase_ms.items())
+        + f"; step {ms_per_step * 1e3:.1f} us")
 
     step_bytes, step_flops = step_work(d, T, U_mean)
     dom = max(phase_ms, key=phase_ms.get)
-    dbytes, dflops = phase_work(d, T, U_mean, dom)   # U: routed experts; shared added inside
+    if dom == "decode_fused":
+        dbytes, dflops = step_work(d, T, U_mean)
+    else:
+        dbytes, dflops = phase_work(d, T, U_mean, dom)   # U: routed experts; shared added inside
     dsec = phase_ms[dom] * 1e-3
     mfma_bound = wl.name == "zipf16384"
     if mfma_bound:
@@ -252,7 +256,6 @@ def main():
         "attainable_frac": round(min(step_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                                      step_bytes / (HBM_PEAK_GBS * 1e9)) / sec, 4),
         "phase_us": {k: round(v * 1e3, 2) for k, v in phase_ms.items()},
-        "untraced_ms_per_step": round(plain_ms_per_step, 5),
     }
 
     result = {

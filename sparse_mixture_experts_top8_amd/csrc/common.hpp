@@ -33,10 +33,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float siluf_(float z) { return z / (1.0f + __expf(-z)); }
 
+// ---- wavefront reductions on DPP lane moves (no LDS traffic) ----
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror and row_mirror
+// combine lanes inside each 16-lane row (after the four steps every lane of a
+// row holds the row's result); the four row results are then read into
+// scalar registers and combined, so every lane returns the same value.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+__device__ __forceinline__ float row_lane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (row_lane_f(v, 0) + row_lane_f(v, 16)) + (row_lane_f(v, 32) + row_lane_f(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(row_lane_f(v, 0), row_lane_f(v, 16)), fmaxf(row_lane_f(v, 32), row_lane_f(v, 48)));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x141>(v));
+  v = min(v, dpp_i<0x140>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Arg-max over the wave under the order (higher value, then lower index):
+// lane-local candidates (bv, bi) in, the winner's value and index out (uniform).
+__device__ __forceinline__ void wave_argmax(float bv, int bi, float* v_out, int* i_out) {
+  const float m = wave_max(bv);
+  *i_out = wave_min_i(bv == m ? bi : 0x7FFFFFFF);
+  *v_out = m;
 }
 
 // 16-byte global load/store as four dwords.

@@ -14,6 +14,30 @@ constexpr int kGemmBNW = 128;   // weight rows per tile: gate_up 64 gate + 64 up
 
 __host__ __device__ inline int router_blocks(int64_t T) { return (int)((T + kRouterTokens - 1) / kRouterTokens); }
 
+// Fused decode path (T <= kDecodeMaxT, H <= 2048, I <= 512, Is <= 512).
+constexpr int kDecodeMaxT = 64;
+struct DecodeArgs {
+  LayerArgs L;
+  const bf16_t* x;      // [T, H]
+  int T;
+  int route_only;       // 1: stop after routing and write offsets/perm
+  bf16_t* out;          // [T, H]
+  uint32_t* ctl;        // control block: epoch, counters, error word
+  float* logits;        // [T, E]
+  int32_t* topk_idx;    // [T, K]
+  float* topk_w;        // [T, K]
+  float* gate_s;        // [T]
+  bf16_t* h;            // [T*K, I] per (token, k) pair, routing weight applied
+  bf16_t* h_sh;         // [T, Is]
+  int32_t* offsets_out; // route-only: [E + 1]
+  int32_t* perm_out;    // route-only: [T*K]
+  unsigned long long epoch;
+};
+constexpr int kDecodeCtlWords = 4 * 32 + 32 * 257;  // one 128-byte line per counter
+
+hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s);
+int decode_max_grid(int num_cus);
+
 hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
                          float* logits_out, hipStream_t s);
 hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s);

@@ -3,13 +3,16 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <chrono>
+#include <unistd.h>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <algorithm>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.hpp"
 
 using moe::bf16_t;
@@ -80,6 +83,62 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   return c;
 }
 
+// The fused decode path serves small batches of the supported shapes.
+bool use_decode(const moe_layer_t* L, int64_t T) {
+  return T >= 1 && T <= moe::kDecodeMaxT && L->hidden <= 2048 && L->expert_inner <= 512 &&
+         L->shared_inner <= 512;
+}
+
+struct DecodeCarve {
+  uint32_t* ctl;
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  float* gate_s;
+  bf16_t* h;
+  bf16_t* h_sh;
+  size_t bytes;
+};
+
+DecodeCarve carve_decode(const moe_layer_t* L, int64_t T, char* base) {
+  const size_t E = L->num_experts, K = L->top_k, I = L->expert_inner, Is = L->shared_inner;
+  const size_t t = (size_t)T, tk = t * K;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  DecodeCarve c{};
+  c.ctl = (uint32_t*)take(moe::kDecodeCtlWords * 4);
+  c.logits = (float*)take(t * E * 4);
+  c.topk_idx = (int32_t*)take(tk * 4);
+  c.topk_w = (float*)take(tk * 4);
+  c.gate_s = (float*)take(t * 4);
+  c.h = (bf16_t*)take(tk * I * 2);
+  c.h_sh = (bf16_t*)take(t * Is * 2);
+  c.bytes = off;
+  return c;
+}
+
+size_t workspace_need(const moe_layer_t* L, int64_t T) {
+  return use_decode(L, T) ? carve_decode(L, T, nullptr).bytes : carve(L, T, nullptr).bytes;
+}
+
+// Call-unique epochs for the decode path's start protocol: a per-process
+// sequence started from the clock and the process id.
+std::atomic<unsigned long long> g_epoch{0};
+std::once_flag g_epoch_once;
+unsigned long long next_epoch() {
+  std::call_once(g_epoch_once, [] {
+    const unsigned long long t = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    g_epoch.store((t << 16) ^ ((unsigned long long)getpid() << 44) ^ 0x9E3779B97F4A7C15ull);
+  });
+  unsigned long long e = ++g_epoch;
+  if (e == 0) e = ++g_epoch;
+  return e;
+}
+
 moe::LayerArgs layer_args(const moe_layer_t* L) {
   moe::LayerArgs a;
   a.H = L->hidden;
@@ -114,11 +173,12 @@ struct DeviceInfo {
   std::once_flag once;
   bool ok = false;
   int cus = 0;
+  int decode_grid = 0;
   char arch[64] = {0};
 };
 DeviceInfo g_dev[64];
 
-int device_check(int* cus) {
+int device_check(int* cus, int* decode_grid = nullptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
@@ -130,10 +190,12 @@ int device_check(int* cus) {
       std::strncpy(d.arch, prop.gcnArchName, sizeof d.arch - 1);
       d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
       d.cus = prop.multiProcessorCount;
+      if (d.ok) d.decode_grid = std::min(d.cus, moe::decode_max_grid(d.cus));
     }
   });
   if (!d.ok) return fail(MOE_ERR_DEVICE, "device %d is '%s', not gfx950", dev, d.arch);
   *cus = d.cus;
+  if (decode_grid) *decode_grid = d.decode_grid;
   return MOE_OK;
 }
 
@@ -142,13 +204,29 @@ int launch_status(hipError_t e, const char* what) {
   return MOE_OK;
 }
 
+moe::DecodeArgs decode_args(const moe_layer_t* L, const void* x, int64_t T, const DecodeCarve& c) {
+  moe::DecodeArgs a{};
+  a.L = layer_args(L);
+  a.x = (const bf16_t*)x;
+  a.T = (int)T;
+  a.ctl = c.ctl;
+  a.logits = c.logits;
+  a.topk_idx = c.topk_idx;
+  a.topk_w = c.topk_w;
+  a.gate_s = c.gate_s;
+  a.h = c.h;
+  a.h_sh = c.h_sh;
+  a.epoch = next_epoch();
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_layer_t* L, int64_t T) {
   if (check_dims(L, T) != MOE_OK || T <= 0) return 0;
-  return carve(L, T, nullptr).bytes;
+  return workspace_need(L, T);
 }
 
 int moe_validate(const moe_layer_t* L, const void* x, int64_t T, const void* out, const void* ws,
@@ -163,7 +241,7 @@ int moe_validate(const moe_layer_t* L, const void* x, int64_t T, const void* out
   if (!aligned16(x)) return fail(MOE_ERR_ALIGN, "x is not 16-byte aligned");
   if (!aligned16(out)) return fail(MOE_ERR_ALIGN, "out is not 16-byte aligned");
   if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
-  const size_t need = carve(L, T, nullptr).bytes;
+  const size_t need = workspace_need(L, T);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T = %lld", ws_bytes, need, (long long)T);
   return MOE_OK;
@@ -181,11 +259,23 @@ int moe_route(const moe_layer_t* L, const void* x, int64_t T, int32_t* topk_idx,
   const void* ptrs[8] = {x, topk_idx, topk_w, offsets, perm, ws, shared_gate, logits};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(MOE_ERR_ALIGN, "a pointer argument is not 16-byte aligned");
+  const size_t need = workspace_need(L, T);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T = %lld", ws_bytes, need, (long long)T);
+  int cus = 0, dgrid = 0;
+  if ((rc = device_check(&cus, &dgrid)) != MOE_OK) return rc;
+  if (use_decode(L, T)) {
+    moe::DecodeArgs a = decode_args(L, x, T, carve_decode(L, T, (char*)ws));
+    a.route_only = 1;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    if (shared_gate) a.gate_s = shared_gate;
+    if (logits) a.logits = logits;
+    a.offsets_out = offsets;
+    a.perm_out = perm;
+    return launch_status(moe::launch_decode(a, dgrid, (hipStream_t)stream), "decode (route)");
+  }
   Carve c = carve(L, T, (char*)ws);
-  if (ws_bytes < c.bytes)
-    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T = %lld", ws_bytes, c.bytes, (long long)T);
-  int cus = 0;
-  if ((rc = device_check(&cus)) != MOE_OK) return rc;
   moe::Work w = c.w;
   w.topk_idx = topk_idx;
   w.topk_w = topk_w;
@@ -202,17 +292,25 @@ int moe_forward_traced(const moe_layer_t* L, const void* x, int64_t T, void* out
                        size_t ws_bytes, void* stream, void* const* events) {
   int rc = moe_validate(L, x, T, out, ws, ws_bytes);
   if (rc != MOE_OK || T == 0) return rc;
-  int cus = 0;
-  if ((rc = device_check(&cus)) != MOE_OK) return rc;
-  const moe::Work w = carve(L, T, (char*)ws).w;
-  const moe::LayerArgs a = layer_args(L);
+  int cus = 0, dgrid = 0;
+  if ((rc = device_check(&cus, &dgrid)) != MOE_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
-  const int t = (int)T;
   auto mark = [&](int i) -> int {
     if (!events) return MOE_OK;
     return launch_status(hipEventRecord((hipEvent_t)events[i], s), "hipEventRecord");
   };
   if ((rc = mark(0)) != MOE_OK) return rc;
+  if (use_decode(L, T)) {
+    moe::DecodeArgs da = decode_args(L, x, T, carve_decode(L, T, (char*)ws));
+    da.out = (bf16_t*)out;
+    if ((rc = launch_status(moe::launch_decode(da, dgrid, s), "decode")) != MOE_OK) return rc;
+    for (int i = 1; i <= 5; ++i)
+      if ((rc = mark(i)) != MOE_OK) return rc;
+    return MOE_OK;
+  }
+  const moe::Work w = carve(L, T, (char*)ws).w;
+  const moe::LayerArgs a = layer_args(L);
+  const int t = (int)T;
   if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, t, w, nullptr, s), "router")) != MOE_OK) return rc;
   if ((rc = mark(1)) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_dispatch(a, t, w, s), "dispatch")) != MOE_OK) return rc;
