@@ -111,6 +111,25 @@ def phase_work(d, T, U, phase):
     raise KeyError(phase)
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE runs scaled by a plain-copy
+    calibration), or None when there is none or the kernel's source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload, {}).get(kernel)
+    if not rec:
+        return None
+    csrc = os.path.join(ROOT, "sparse_mixture_experts_top8_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (rec["source"], "common.hpp", "kernels.hpp"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return int(rec["traffic_bytes"]) if h.hexdigest()[:16] == rec["source_sha"] else None
+
+
 def step_work(d, T, U):
     """Algorithmic bytes and flops of one whole layer call."""
     per_expert = 2 * 3 * d.H * d.I
@@ -223,9 +242,12 @@ def main():
     torch.cuda.synchronize()
     phase_ms = {p: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
                 for j, p in enumerate(moe.PHASES)}
-    fused = T <= 64 and d.H <= 2048 and d.I <= 512 and d.Is <= 512
+    fused = T <= 16 and d.H <= 2048 and d.I <= 512 and d.Is <= 512
     if fused:
-        phase_ms = {"decode_fused": phase_ms["router"]}
+        # One kernel per step: its average launch duration is the timed
+        # region divided by the steps (events around each launch would add
+        # their own marker overhead to a ~30 us kernel).
+        phase_ms = {"decode_fused": ms_per_step}
     log("phase us: " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in phase_ms.items())
         + f"; step {ms_per_step * 1e3:.1f} us")
 
@@ -246,7 +268,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     roof.update({"kernel": dom, "kernel_us": round(phase_ms[dom] * 1e3, 2),
-                 "alg_bytes_per_launch": int(dbytes), "alg_flops_per_launch": int(dflops), "traffic": None})
+                 "alg_bytes_per_launch": int(dbytes), "alg_flops_per_launch": int(dflops),
+                 "traffic": measured_traffic(wl.name, dom)})
 
     sec = ms_per_step * 1e-3
     layer_stats = {

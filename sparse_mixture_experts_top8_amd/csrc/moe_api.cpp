@@ -83,9 +83,12 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   return c;
 }
 
-// The fused decode path serves small batches of the supported shapes.
+// The fused decode path serves small batches of the supported shapes; above
+// kDecodePathMaxT tokens the grouped-GEMM path is faster (the fused kernel
+// handles up to kDecodeMaxT and is exercised there by its own limit).
+constexpr int64_t kDecodePathMaxT = 16;
 bool use_decode(const moe_layer_t* L, int64_t T) {
-  return T >= 1 && T <= moe::kDecodeMaxT && L->hidden <= 2048 && L->expert_inner <= 512 &&
+  return T >= 1 && T <= kDecodePathMaxT && L->hidden <= 2048 && L->expert_inner <= 512 &&
          L->shared_inner <= 512;
 }
 

@@ -108,11 +108,11 @@ def run_layer(layer, xb, want_logits=False):
     ws = layer.workspace(T)
     r = moe.route(x, layer, ws=ws, want_logits=want_logits)
     torch.cuda.synchronize()
-    if T <= 64:
+    if T <= 16:
         assert decode_error_word(ws) == 0, "decode path wait timed out (route)"
     out = moe.forward(x, layer, ws=ws)
     torch.cuda.synchronize()
-    if T <= 64:
+    if T <= 16:
         assert decode_error_word(ws) == 0, "decode path wait timed out (forward)"
     return r, out
 
