@@ -1,6 +1,6 @@
-// Fused decode path of the MoE layer for small batches (T <= 64 tokens) on
-// gfx950: one persistent, co-resident launch that streams only the weights
-// of the experts the tokens select.
+// Fused decode path of the MoE layer for small batches (1 <= T <= 16 tokens)
+// on gfx950: one launch, one workgroup per CU, that streams only the weights of
+// the experts the tokens select.
 //
 // Definition of the layer: "Qwen3.6-35B-A3B — Architecture Overview", section
 // "MoE FFN: 256 Experts" (router Linear, softmax, top-8 renormalised; SwiGLU
@@ -9,47 +9,48 @@
 // Step": the router decides which expert weights a token needs at all, so a
 // decode step only has to read those.
 //
-// Phases, chained through device-scope counters in the workspace (no host
-// round trip, no second launch):
-//   A  router: tasks of 4 router rows (the last one also the shared-expert
-//      gate row) x all tokens; shared expert gate/up: tasks of 16 inner rows.
-//      Router tasks publish fp32 logits (and the shared gate scalar).
-//   K  top-K per token: for T <= kLocalTopkT every workgroup selects all
-//      tokens' experts itself from the published logits (one hand-off less);
-//      otherwise workgroup t selects token t's and publishes them.
-//   L  each workgroup builds, in LDS, the list of touched experts and each
-//      expert's (token, k) pairs in pair-id order (the same stable grouping
-//      as the counting sort).
-//   B  routed gate/up: tasks of (touched expert, 16 inner rows) applied to the
-//      tokens routed to that expert; h = w * SiLU(x.Wg) * (x.Wu) is published
-//      in bf16 per (token, k) pair, already scaled by the routing weight.
-//   C  down + combine: each workgroup owns 8 output rows; its waves split the
-//      experts (touched ones, then the shared expert), each accumulating
-//      W_down[rows] . h into a tile with the tokens as columns, so the
-//      weighted sum over experts happens inside the MFMA accumulators; the
-//      four wave tiles are added in LDS in a fixed order (no float atomics,
-//      bitwise reproducible).
+// Phases (no host round trip, no second launch):
+//   A  every workgroup computes its share of the router rows (the shared-expert
+//      gate row is router row E) and of the shared expert's gate/up rows for
+//      all tokens; it publishes its logits tagged with the call's tag, and
+//      h_sh = sigma(x . w_g) * SiLU(g) * u (it evaluates the gate row itself).
+//   K  every workgroup polls the tagged logits until all carry this call's
+//      tag (the data is its own completion flag) and selects every token's
+//      top-K.
+//   L  every workgroup builds, in LDS, the touched-expert list and each
+//      expert's (token, k) pairs in pair-id order (the counting-sort order).
+//   B  routed gate/up in blocks of (expert, 8 inner rows); h = w * SiLU(g) * u
+//      is published in bf16 per pair, routing weight applied.   [grid hand-off]
+//   C  down projection + combine, output-row stationary: each workgroup owns a
+//      few output rows and adds W_down[e][rows] . h over the shared expert and
+//      every touched expert, in a fixed order, then writes out.
 //
-// Every task is a 16-row x 16-column tile on v_mfma_f32_16x16x32_bf16 (rows:
-// weight rows, columns: tokens), with the hidden dimension split across the
-// four waves and their partial tiles summed in LDS; no cross-lane
-// reductions and no unrolled straight-line code beyond one task's loads
-// (the whole kernel stays far below the instruction-cache size).
+// Weight streams are software pipelined: a wave keeps the loads of the next
+// blocks (phase B) or groups (phase C) in flight while it computes the current
+// one, and the down-projection weights of the first groups are requested before
+// hand-off B, since they do not depend on h.  Every tile is a 16 x 16 tile of
+// v_mfma_f32_16x16x32_bf16 whose columns are tokens (or one expert's pairs),
+// with the contraction split over the four waves; partial tiles meet in LDS in
+// a fixed order, so results are bitwise reproducible.
 //
 // Cross-workgroup data on MI355X: each XCD has its own write-back L2, and the
 // agent-scope release/acquire fences that keep plain stores coherent across
-// XCDs are L2 write-backs and invalidates, far too costly to issue per task.
-// Instead every value one workgroup hands to another is written and read with
-// agent-scope atomic accesses (write-through to, and read from, the device
-// coherence point); a wave publishes by waiting for its stores to complete
-// (s_waitcnt) and then bumping a counter, and readers poll counters with
-// agent-scope loads.  Weights and x are never written and use plain loads.
+// XCDs are L2 write-backs and invalidates, far too costly per hand-off.  Every
+// value one workgroup hands to another is written with agent-scope
+// (write-through) stores and read with device-scope buffer loads (sc1).  For
+// the h hand-off a workgroup arrives once all its waves' stores have completed
+// (s_waitcnt), by one atomic increment of its XCD's counter (eight counters on
+// separate 128-byte lines, so arrivals do not serialise on one address);
+// waiters poll the eight counters with one load.  The logits need no counter:
+// each is published as one 64-bit store of (value, tag).
 //
-// Start protocol: the host passes a call-unique 64-bit epoch.  Workgroup 0
-// zeroes the counters and then publishes the epoch; every other workgroup
-// sees the epoch before it touches a counter, so stale values from an earlier
-// call are never read.  Every wait is bounded in time (see wait_until), so
-// the grid always drains.
+// Start protocol: the host passes a call-unique 64-bit epoch (low word never
+// 0, the tag).  Workgroup 0 zeroes the counters and then publishes the epoch;
+// every other workgroup sees the epoch before it touches a counter, so stale
+// values from an earlier call are never read.  Every wait is bounded in time
+// (see wait_until), so the grid always drains.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace moe {
@@ -58,30 +59,29 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxKSteps = 16;       // 32-wide k-steps in one wave's quarter of H (H <= 2048)
-constexpr int kDownRows = 8;         // output rows of one down tile
-constexpr int kDownGroups = 8;       // experts per down batch
-constexpr int kDownKSteps = 4;       // 32-wide k-steps of the inner dimension per wave (inner <= 512)
-constexpr int kLocalTopkT = 16;      // up to this many tokens every workgroup runs the top-K itself
+constexpr int kMaxT = kDecodeMaxT;       // tokens (columns of every tile)
+constexpr int kMaxHSteps = 16;           // 32-wide k-steps in one wave's quarter of H (H <= 2048)
+constexpr int kMaxISteps = 4;            // 32-wide k-steps in one wave's quarter of an inner dim (<= 512)
+constexpr int kXStride = 2048 + 8;       // LDS row stride of x, bf16 elements (rows stay 16-byte aligned)
+constexpr int kBDepth = 2;               // gate/up blocks in flight per wave
+constexpr int kCDepth = 6;               // down groups in flight per wave
 constexpr unsigned long long kWaitTicks = 25000000ull;  // 0.25 s of the 100 MHz clock
 
-// Control block layout (uint32 words); every counter has its own 128-byte
-// line so that pollers of one counter do not queue behind another's.
-constexpr int kLine = 32;                  // words per 128-byte line
-constexpr int kCtlEpoch = 0;               // 64-bit epoch in words 0-1
-constexpr int kCtlError = 1 * kLine;       // nonzero after a timed-out wait
-constexpr int kCtlLogits = 2 * kLine;      // router rows published
-constexpr int kCtlTopk = 3 * kLine;        // tokens whose top-K is published
-constexpr int kCtlH = 4 * kLine;           // + kLine * g: inner rows of h finished for group g (E = shared)
-static_assert(kDecodeCtlWords >= kCtlH + kLine * 257, "control block too small");
+// Control block layout (uint32 words); every counter has its own 128-byte line.
+constexpr int kLine = 32;                // words per 128-byte line
+constexpr int kCtlEpoch = 0;             // 64-bit epoch in words 0-1
+constexpr int kCtlError = 1 * kLine;     // nonzero after a timed-out wait
+constexpr int kCtlBarB = 2 * kLine;      // + kLine * x: arrivals at the h hand-off from XCD x
+static_assert(kDecodeCtlWords >= 10 * kLine, "control block too small");
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
 // Weights are read once per call: non-temporal loads keep them from evicting
-// the kernel's code and the small hot data (x, h, counters) from the caches.
+// the small hot data (x, h, counters) from the caches.
 __device__ __forceinline__ u32x4 ldw(const bf16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+__device__ __forceinline__ u32x4 ld_lds16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -91,32 +91,35 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ uint32_t ld_cnt(uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_dev(float* p, float v) {
+template <typename V>
+__device__ __forceinline__ void st_dev(V* p, V v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_dev(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Published data (written by other workgroups with write-through stores) is
-// read with device-scope buffer loads (sc1): they bypass any XCD-local cached
-// copy, so no L2 invalidate is needed after a hand-off.  Buffer loads past the
-// resource's size return zero, which masks fragments without a branch.
+// Published data is read with device-scope buffer loads (sc1): they bypass any
+// XCD-local cached copy, so no L2 invalidate is needed after a hand-off.
+// Buffer loads past the resource's size return zero, which masks fragments
+// without a branch.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutside = 0x80000000u;   // out of range even after adding a k offset
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ u32x4 ld_pub16(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
-}
 __device__ __forceinline__ float ld_pub_f(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16));
 }
-__device__ __forceinline__ int ld_pub_i(rsrc_t r, uint32_t off) {
-  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16);
+// h after its hand-off: an ordinary (L2-cacheable) load.  No CU reads h
+// before the hand-off in a call, and the caches hold no copies from earlier
+// launches, so the first reader in each XCD fetches the written-through data
+// and the XCD's other workgroups hit in its L2.
+__device__ __forceinline__ u32x4 ld_after16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+// Weight fragment through a buffer resource, non-temporal; an offset outside
+// the resource returns zeros without touching memory, so pipeline stages past
+// the end of the work and k-steps past the contraction are issued
+// unconditionally (the load counter then matches in every path) and add zero.
+__device__ __forceinline__ u32x4 ldw_buf(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
 }
 
 // All of this wave's earlier memory operations have completed (stores at the
@@ -137,8 +140,10 @@ __device__ __forceinline__ void wait_until(Ready ready, uint32_t* err, uint32_t 
     const unsigned long long t0 = wall_clock64();
     uint32_t n = 0;
     while (!ready()) {
-      __builtin_amdgcn_s_sleep(2);
-      if ((++n & 31u) == 0u && (ld_cnt(err) != 0u || wall_clock64() - t0 > kWaitTicks)) {
+      // A short back-off: every workgroup polls the same few lines, and
+      // tighter polling only queues more requests in front of the writes.
+      __builtin_amdgcn_s_sleep(4);
+      if ((++n & 63u) == 0u && (ld_cnt(err) != 0u || wall_clock64() - t0 > kWaitTicks)) {
         __hip_atomic_fetch_or(err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -147,43 +152,68 @@ __device__ __forceinline__ void wait_until(Ready ready, uint32_t* err, uint32_t 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Top-K of one token's published logits by one wave: descending logit, ties to
-// the lower expert index; lane k < K receives the k-th index and its weight,
-// the softmax over the selected logits (equal to the full softmax renormalised).
-__device__ __noinline__ void topk_token(rsrc_t logits, int t, int E, int K, int lane, int* idx_out, float* w_out) {
-  float v[4];
+// Wave-wide inclusive prefix sum (DPP shifts inside each 16-lane row, then the
+// row totals are added from scalar registers).
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
+// Top-K of NT tokens by one wave (independent chains, interleaved), from each
+// lane's four logits of experts 4 lane + c: descending logit, ties to the
+// lower expert index (the lowest lane among equal lane bests, the lowest c
+// inside a lane); lane k < K receives the k-th index and its weight, the
+// softmax over the selected logits (equal to the full softmax renormalised).
+// A validity mask (experts < E, not yet taken) keeps every pick distinct even
+// among equal or -inf values; NaN counts as -inf.
+template <int NT>
+__device__ __forceinline__ void topk_select(const float (&lv)[NT][4], int E, int K, int lane, int (&idx_out)[NT],
+                                            float (&w_out)[NT]) {
+  float v[NT][4];
+  uint32_t valid[NT];
+  float vmax[NT], den[NT], mine_v[NT];
+  int mine_i[NT];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int e = lane + 64 * c;
-    v[c] = ld_pub_f(logits, 4u * (uint32_t)(t * E + min(e, E - 1)));
+  for (int j = 0; j < NT; ++j) {
+    valid[j] = 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[j][c] = lv[j][c] == lv[j][c] ? lv[j][c] : -INFINITY;
+      if (4 * lane + c < E) valid[j] |= 1u << c;
+    }
+    vmax[j] = 0.f;
+    den[j] = 0.f;
+    mine_v[j] = 0.f;
+    mine_i[j] = 0;
   }
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    if (lane + 64 * c >= E || v[c] != v[c]) v[c] = -INFINITY;
-  float vmax = 0.f, den = 0.f, mine_v = 0.f;
-  int mine_i = 0;
   for (int k = 0; k < K; ++k) {
-    // Lane-local best (strict > keeps the lower column on ties); padding
-    // columns hold -inf and lose every tie to a real expert.
-    float bv = v[0];
-    int bi = lane;
 #pragma unroll
-    for (int c = 1; c < 4; ++c)
-      if (v[c] > bv) { bv = v[c]; bi = lane + 64 * c; }
-    float wv;
-    int wi;
-    wave_argmax(bv, bi, &wv, &wi);
-    if ((wi & 63) == lane) {
+    for (int j = 0; j < NT; ++j) {
+      float bv = -INFINITY;
+      int bc = -1;
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if ((wi >> 6) == c) v[c] = -INFINITY;
+        if (((valid[j] >> c) & 1u) && (bc < 0 || v[j][c] > bv)) { bv = v[j][c]; bc = c; }
+      const float mx = wave_max(bv);
+      const unsigned long long win = __ballot(bc >= 0 && bv == mx);
+      const int wl = (int)__builtin_ctzll(win);
+      const int wc = __builtin_amdgcn_readlane(bc, wl);
+      if (lane == wl) valid[j] &= ~(1u << wc);
+      if (k == 0) vmax[j] = mx;
+      den[j] += __expf(mx - vmax[j]);
+      if (lane == k) { mine_v[j] = mx; mine_i[j] = 4 * wl + wc; }
     }
-    if (k == 0) vmax = wv;
-    den += __expf(wv - vmax);
-    if (lane == k) { mine_v = wv; mine_i = wi; }
   }
-  *idx_out = clamp_expert(mine_i, E);
-  *w_out = __expf(mine_v - vmax) / den;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    idx_out[j] = clamp_expert(mine_i[j], E);
+    w_out[j] = __expf(mine_v[j] - vmax[j]) / den[j];
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
@@ -191,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int H = L.H, E = L.E, K = L.K, I = L.I, Is = L.Is, T = a.T;
   const int TK = T * K;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int G = gridDim.x;
+  const int G = gridDim.x, wg = blockIdx.x;
   const int m = lane & 15;            // A-operand row / B-operand column of this lane
   const int kq = (lane >> 4) * 8;     // this lane's 8 elements inside a 32-wide k-step
   const int nks = H / 128;            // k-steps in this wave's quarter of H
@@ -199,31 +229,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   uint32_t* ctl = a.ctl;
   uint32_t* err = ctl + kCtlError;
   unsigned long long* epoch_p = reinterpret_cast<unsigned long long*>(ctl + kCtlEpoch);
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   const f32x4 zf4 = {0.f, 0.f, 0.f, 0.f};
-  const rsrc_t r_logits = make_rsrc(a.logits, (size_t)T * E * 4);
 
-  __shared__ int s_cnt[257];
-  __shared__ int s_off[258];
-  __shared__ int s_cur[257];
-  __shared__ int s_list[kDecodeMaxT * 8];
-  __shared__ int s_tidx[kDecodeMaxT * 8];
-  __shared__ float s_tw[kDecodeMaxT * 8];
-  __shared__ int s_touched[257];
-  __shared__ int s_ntouched;
-  __shared__ float s_red[kWaves][4][256];   // per wave: up to four 16x16 partial tiles
+  __shared__ __attribute__((aligned(16))) bf16_t s_x[kMaxT * kXStride];   // x, one padded row per token
+  __shared__ f32x4 s_red[2][kWaves][kWave];     // partial tiles of the four waves (two blocks in flight)
+  __shared__ float s_acc[kWaves][16][kMaxT];    // phase C: per-wave output accumulators
+  __shared__ uint32_t s_mask[256];              // tokens that selected expert e (bit t)
+  __shared__ int s_off[257];                    // pair-list offsets per expert
+  __shared__ int s_touched[256];                // touched experts, ascending
+  __shared__ int s_list[kMaxT * 8];             // pair ids grouped by expert, pair-id order inside
+  __shared__ int s_tidx[kMaxT * 8];
+  __shared__ float s_tw[kMaxT * 8];
+  __shared__ int s_vg[256 + kMaxT * 8 / 8];    // routed chunks: (u << 16) | (first pair << 8) | pairs (<= 8)
+  __shared__ int s_U, s_NV;
 
   // ---------------- start: counters zeroed, then the epoch published ----------------
-  // Workgroup 0's threads zero one counter word each, then thread 0 publishes
-  // the epoch once every store has completed.
-  if (blockIdx.x == 0) {
-    for (int i = tid; i < 3 + E + 1; i += kThreads)
+  if (wg == 0) {
+    for (int i = tid; i < 9; i += kThreads)
       __hip_atomic_store(ctl + kCtlError + kLine * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     stores_complete();
     __syncthreads();
     if (tid == 0) __hip_atomic_store(epoch_p, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  bool epoch_seen = false;
+  const uint32_t tag = (uint32_t)a.epoch;
+  bool epoch_seen = false;   // meaningful in wave 0
   auto see_epoch = [&]() {
     if (!epoch_seen) {
       wait_until([&] { return __hip_atomic_load(epoch_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch; },
@@ -231,241 +260,195 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       epoch_seen = true;
     }
   };
-  // Every wave's stores are complete, then thread 0 counts n arrivals.
-  auto publish = [&](uint32_t* cnt, uint32_t n) {
-    stores_complete();
+
+  for (int i = tid; i < 256; i += kThreads) s_mask[i] = 0u;
+  for (int i = tid; i < kWaves * 16 * kMaxT; i += kThreads) (&s_acc[0][0][0])[i] = 0.f;
+
+  // ---------------- phase A: router rows and shared-expert rows ----------------
+  // Workgroup wg owns router rows [r_lo, r_hi) of E + 1 (row E: the shared
+  // gate) and shared inner rows [s_lo, s_hi).  Tile rows: the router rows, the
+  // shared gate row (when it owns inner rows), then (gate, up) row pairs; the
+  // host guarantees they fit one 16-row tile.  The weight loads go out first,
+  // then x is staged in LDS (every workgroup keeps all of x there).
+  {
+    const int r_lo = (int)((long long)wg * (E + 1) / G), r_hi = (int)((long long)(wg + 1) * (E + 1) / G);
+    const int s_lo = (int)((long long)wg * Is / G), s_hi = (int)((long long)(wg + 1) * Is / G);
+    const int n_r = r_hi - r_lo, n_s = s_hi - s_lo;
+    const int p0 = n_r + (n_s > 0 ? 1 : 0);            // first (gate, up) pair row
+    const int nrow = p0 + 2 * n_s;
+    u32x4 af[kMaxHSteps];
+    if (nrow > 0) {
+      const int mr = min(m, nrow - 1);
+      const bf16_t* rp;
+      if (mr < n_r) {
+        const int e = r_lo + mr;
+        rp = e < E ? L.router_w + (size_t)e * H : L.sh_expert_gate;
+      } else if (mr < p0) {
+        rp = L.sh_expert_gate;
+      } else {
+        const int p = (mr - p0) >> 1;
+        rp = (((mr - p0) & 1) ? L.sh_up_w : L.sh_gate_w) + (size_t)(s_lo + p) * H;
+      }
+      rp += kbeg + kq;
+#pragma unroll
+      for (int ks = 0; ks < kMaxHSteps; ++ks) af[ks] = ldw(rp + 32 * min(ks, nks - 1));
+    }
+    {
+      const int cpr = H / 8;   // 16-byte chunks per row of x
+      u32x4 xr[kMaxT];
+#pragma unroll
+      for (int j = 0; j < kMaxT; ++j) {
+        const int i = tid + j * kThreads;
+        if (i < T * cpr) {
+          const int t = i / cpr;
+          xr[j] = ld16(a.x + (size_t)t * H + 8 * (i - t * cpr));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxT; ++j) {
+        const int i = tid + j * kThreads;
+        if (i < T * cpr) {
+          const int t = i / cpr;
+          *reinterpret_cast<u32x4*>(s_x + t * kXStride + 8 * (i - t * cpr)) = xr[j];
+        }
+      }
+    }
     __syncthreads();
-    if (wave == 0) {
-      see_epoch();
-      if (lane == 0) __hip_atomic_fetch_add(cnt, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  };
-
-  // Gate/up task: rows [inner0, inner0 + R) of group g's gate and up
-  // projections (g == E: the shared expert) against the tokens of the group,
-  // h = SiLU(gate) * up, scaled by the routing weight for routed experts,
-  // stored as bf16 pairs.  R is even and at most 16.
-  auto gate_up_task = [&](int g, int inner0, int R) {
-    // Loads are unconditional: tile rows >= R repeat row R - 1 and columns
-    // beyond the group's tokens repeat its first token; those outputs are
-    // never used.  k-steps beyond H / 128 repeat the last one and are skipped.
-    const bool sh = g == E;
-    const int mr = min(m, R - 1);
-    const size_t grow = sh ? (size_t)(inner0 + mr) * H : ((size_t)g * 2 * I + inner0 + mr) * H;
-    const size_t urow = sh ? (size_t)(inner0 + mr) * H : ((size_t)g * 2 * I + I + inner0 + mr) * H;
-    const bf16_t* gp = (sh ? L.sh_gate_w : L.gate_up_w) + grow + kbeg + kq;
-    const bf16_t* up = (sh ? L.sh_up_w : L.gate_up_w) + urow + kbeg + kq;
-    u32x4 ag[kMaxKSteps], au[kMaxKSteps];
+    if (nrow > 0) {
+      const bf16_t* xs = s_x + min(m, T - 1) * kXStride + kbeg + kq;
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+      u32x4 xb[kMaxHSteps];
 #pragma unroll
-    for (int ks = 0; ks < kMaxKSteps; ++ks) {
-      const int kk = 32 * min(ks, nks - 1);
-      ag[ks] = ldw(gp + kk);
-      au[ks] = ldw(up + kk);
-    }
-    const int p0 = sh ? 0 : s_off[g];
-    const int ncol = sh ? T : s_off[g + 1] - p0;
-    for (int cb = 0; cb < ncol; cb += 16) {
-      const int c = min(cb + m, ncol - 1);
-      const int tok = sh ? c : s_list[p0 + c] / K;
-      const bf16_t* xp = a.x + (size_t)tok * H + kbeg + kq;
-      u32x4 xf[kMaxKSteps];
+      for (int ks = 0; ks < kMaxHSteps; ++ks) xb[ks] = ks < nks ? ld_lds16(xs + 32 * ks) : z4;
+      f32x4 d = zf4;
 #pragma unroll
-      for (int ks = 0; ks < kMaxKSteps; ++ks) xf[ks] = ld16(xp + 32 * min(ks, nks - 1));
-      f32x4 dg = zf4, du = zf4;
-#pragma unroll
-      for (int ks = 0; ks < kMaxKSteps; ++ks) {
-        if (ks < nks) {
-          dg = mfma16(ag[ks], xf[ks], dg);
-          du = mfma16(au[ks], xf[ks], du);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s_red[wave][0][(4 * (lane >> 4) + r) * 16 + m] = dg[r];
-        s_red[wave][1][(4 * (lane >> 4) + r) * 16 + m] = du[r];
-      }
+      for (int ks = 0; ks < kMaxHSteps; ++ks) d = mfma16(af[ks], xb[ks], d);
+      s_red[0][wave][lane] = d;
       __syncthreads();
-      // Thread: inner rows i0, i0 + 1 of column cc.
-      if (tid < 128) {
-        const int i0 = 2 * (tid >> 4), cl = tid & 15, cc = cb + cl;
-        if (i0 < R && cc < ncol) {
-          float hv[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int idx = (i0 + j) * 16 + cl;
-            const float gs = (s_red[0][0][idx] + s_red[1][0][idx]) + (s_red[2][0][idx] + s_red[3][0][idx]);
-            const float us = (s_red[0][1][idx] + s_red[1][1][idx]) + (s_red[2][1][idx] + s_red[3][1][idx]);
-            hv[j] = siluf_(gs) * us;
-          }
-          bf16_t* dst;
-          if (sh) {
-            dst = a.h_sh + (size_t)cc * Is + inner0 + i0;
+      // Thread (row mm, column n) of the summed tile.
+      const int mm = tid >> 4, n = tid & 15;
+      auto tile = [&](int row) {
+        const int ll = (row >> 2) * 16 + n, ii = row & 3;
+        return (s_red[0][0][ll][ii] + s_red[0][1][ll][ii]) + (s_red[0][2][ll][ii] + s_red[0][3][ll][ii]);
+      };
+      if (n < T && mm < nrow) {
+        if (mm < n_r) {
+          const int e = r_lo + mm;
+          const float v = tile(mm);
+          if (e < E) {
+            st_dev(a.logits_t + (size_t)n * E + e, ((uint64_t)__float_as_uint(v) << 32) | tag);
+            if (a.logits_out) a.logits_out[(size_t)n * E + e] = v;
           } else {
-            const int q = s_list[p0 + cc];
-            const float w = s_tw[q];
-            hv[0] *= w;
-            hv[1] *= w;
-            dst = a.h + (size_t)q * I + inner0 + i0;
+            st_dev(a.gate_s + n, sigmoidf_(v));
           }
-          st_dev(reinterpret_cast<uint32_t*>(dst), pack_bf16x2(hv[0], hv[1]));
+        } else if (mm >= p0 && ((mm - p0) & 1) == 0) {
+          const float hv = sigmoidf_(tile(n_r)) * siluf_(tile(mm)) * tile(mm + 1);
+          st_dev(a.h_sh + (size_t)n * Is + s_lo + ((mm - p0) >> 1), (bf16_t)f32_to_bf16(hv));
         }
       }
-      __syncthreads();
-    }
-    publish(ctl + kCtlH + kLine * g, (uint32_t)R);
-  };
-
-  // ---------------- phase A: router rows and shared-expert gate/up rows ----------------
-  const int nR = (E + 1 + 3) / 4;
-  int SR = 2;                                   // shared rows per task: power of two >= Is / G
-  while (SR < 16 && SR * G < Is) SR <<= 1;
-  const int nS = a.route_only ? 0 : Is / SR;
-  for (int task = blockIdx.x; task < nR + nS; task += G) {
-    if (task < nR) {
-      // Router rows 4*task + m (m < 4); row E is the shared-expert gate row.
-      // Tile rows >= 4 (and rows past E) repeat a valid row; ignored below.
-      const int e_row = min(4 * task + min(m, 3), E);
-      const bf16_t* rp = (e_row < E ? L.router_w + (size_t)e_row * H : L.sh_expert_gate) + kbeg + kq;
-      u32x4 af[kMaxKSteps];
-#pragma unroll
-      for (int ks = 0; ks < kMaxKSteps; ++ks) af[ks] = ldw(rp + 32 * min(ks, nks - 1));
-      for (int cb = 0; cb < T; cb += 16) {
-        const int t = min(cb + m, T - 1);
-        const bf16_t* xp = a.x + (size_t)t * H + kbeg + kq;
-        u32x4 xf[kMaxKSteps];
-#pragma unroll
-        for (int ks = 0; ks < kMaxKSteps; ++ks) xf[ks] = ld16(xp + 32 * min(ks, nks - 1));
-        f32x4 d = zf4;
-#pragma unroll
-        for (int ks = 0; ks < kMaxKSteps; ++ks)
-          if (ks < nks) d = mfma16(af[ks], xf[ks], d);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s_red[wave][0][(4 * (lane >> 4) + r) * 16 + m] = d[r];
-        __syncthreads();
-        if (tid < 64) {
-          const int i = tid >> 4, c = tid & 15;
-          const int e = 4 * task + i, tt = cb + c;
-          if (e <= E && tt < T) {
-            const float v = (s_red[0][0][tid] + s_red[1][0][tid]) + (s_red[2][0][tid] + s_red[3][0][tid]);
-            if (e < E) st_dev(a.logits + (size_t)tt * E + e, v);
-            else st_dev(a.gate_s + tt, sigmoidf_(v));
-          }
-        }
-        __syncthreads();
-      }
-      publish(ctl + kCtlLogits, (uint32_t)min(4, E + 1 - 4 * task));
-    } else {
-      gate_up_task(E, SR * (task - nR), SR);
     }
   }
 
   // ---------------- phase K: top-K selections into LDS ----------------
-  if (T <= kLocalTopkT) {
-    // Wave 0 polls; the barrier releases the others.
-    if (wave == 0) {
-      see_epoch();
-      wait_until([&] { return ld_cnt(ctl + kCtlLogits) >= (uint32_t)(E + 1); }, err, 1u);
-    }
-    __syncthreads();
+  // Wave w handles tokens w, w + 4, ... (NT of them, lane: experts 4 lane ..
+  // 4 lane + 3): it polls their tagged logits until every one carries this
+  // call's tag, then selects the top-K of all of them together.
+  {
+    const rsrc_t r_lt = make_rsrc(a.logits_t, (size_t)T * E * 8);
+    auto run = [&](auto nt_tag) {
+      constexpr int NT = decltype(nt_tag)::value;
+      uint64_t sl[NT][4];
+      auto ready = [&] {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int t = wave + kWaves * j;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * lane + c;
+            const bool in = e < E && t < T;
+            // One 64-bit load: value and tag come from the same store.
+            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(r_lt, in ? 8u * (uint32_t)(t * E + e) : kOutside, 0, 16);
+            sl[j][c] = ((uint64_t)w2[1] << 32) | w2[0];
+            ok = ok && (!in || (uint32_t)sl[j][c] == tag);
+          }
+        }
+        return __ballot(!ok) == 0ull;
+      };
+      wait_until(ready, err, 4u);
+      float lv[NT][4];
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lv[j][c] = __uint_as_float((uint32_t)(sl[j][c] >> 32));
+      int ix[NT];
+      float wv[NT];
+      topk_select<NT>(lv, E, K, lane, ix, wv);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int t = wave + kWaves * j;
+        if (t < T && lane < K) { s_tidx[t * K + lane] = ix[j]; s_tw[t * K + lane] = wv[j]; }
+      }
+    };
     if (wave < T) {
-      for (int t = wave; t < T; t += kWaves) {
-        int ix;
-        float wv;
-        topk_token(r_logits, t, E, K, lane, &ix, &wv);
-        if (lane < K) { s_tidx[t * K + lane] = ix; s_tw[t * K + lane] = wv; }
-      }
-    }
-  } else {
-    if (wave == 0 && (int)blockIdx.x < T) {
-      see_epoch();
-      wait_until([&] { return ld_cnt(ctl + kCtlLogits) >= (uint32_t)(E + 1); }, err, 1u);
-      const int t = blockIdx.x;
-      int ix;
-      float wv;
-      topk_token(r_logits, t, E, K, lane, &ix, &wv);
-      if (lane < K) {
-        st_dev(a.topk_idx + (size_t)t * K + lane, ix);
-        st_dev(a.topk_w + (size_t)t * K + lane, wv);
-      }
-      stores_complete();
-      if (lane == 0) __hip_atomic_fetch_add(ctl + kCtlTopk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (wave == 0) {
-      see_epoch();
-      wait_until([&] { return ld_cnt(ctl + kCtlTopk) >= (uint32_t)T; }, err, 1u);
-      const rsrc_t r_ti = make_rsrc(a.topk_idx, (size_t)TK * 4), r_tw = make_rsrc(a.topk_w, (size_t)TK * 4);
-      for (int q = lane; q < TK; q += 64) {
-        s_tidx[q] = clamp_expert(ld_pub_i(r_ti, 4u * q), E);
-        s_tw[q] = ld_pub_f(r_tw, 4u * q);
-      }
+      if (T <= kWaves) run(std::integral_constant<int, 1>{});
+      else if (T <= 2 * kWaves) run(std::integral_constant<int, 2>{});
+      else run(std::integral_constant<int, 4>{});
     }
   }
   __syncthreads();
 
   // ---------------- phase L: per-expert pair lists in LDS ----------------
+  // Token masks per expert, then offsets and the touched list from one scan
+  // (low half: pair counts, high half: touched flags), then each pair's slot:
+  // its expert's offset plus the number of earlier tokens with that expert.
+  for (int q = tid; q < TK; q += kThreads) atomicOr(&s_mask[s_tidx[q]], 1u << (q / K));
+  __syncthreads();
   if (wave == 0) {
-    for (int e = lane; e <= 256; e += 64) s_cnt[e] = 0;
-    __builtin_amdgcn_wave_barrier();
-    for (int q = lane; q < TK; q += 64) atomicAdd(&s_cnt[s_tidx[q]], 1);
-    __builtin_amdgcn_wave_barrier();
-    // Exclusive scan of the E counts (four per lane).
-    int c4[4], run = 0;
+    int v4[4], run = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
-      c4[j] = e < E ? s_cnt[e] : 0;
-      run += c4[j];
+      const int c = e < E ? __popc(s_mask[e]) : 0;
+      v4[j] = c | ((c > 0 ? 1 : 0) << 16);
+      run += v4[j];
     }
-    int incl = run;
+    const int incl = wave_incl_scan(run, lane);
+    // Chunks of at most 8 pairs per touched expert (phase C tiles).
+    int n4[4], nrun = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int n = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += n;
+    for (int j = 0; j < 4; ++j) {
+      n4[j] = ((v4[j] & 0xFFFF) + 7) >> 3;
+      nrun += n4[j];
     }
-    int base = incl - run;
+    const int nincl = wave_incl_scan(nrun, lane);
+    int ex = incl - run, nex = nincl - nrun;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
-      if (e < E) { s_off[e] = base; s_cur[e] = base; }
-      base += c4[j];
-    }
-    if (lane == 63) s_off[E] = incl;
-    __builtin_amdgcn_wave_barrier();
-    // Stable placement: a pair's slot is its expert's cursor plus the number
-    // of earlier lanes in this 64-pair chunk with the same expert.
-    const unsigned long long lt = (1ull << lane) - 1ull;
-    for (int q0 = 0; q0 < TK; q0 += 64) {
-      const int q = q0 + lane;
-      const bool valid = q < TK;
-      const int key = valid ? s_tidx[q] : 511;
-      unsigned long long peers = __ballot(valid);
-#pragma unroll
-      for (int b = 0; b < 9; ++b) {
-        const unsigned long long msk = __ballot((key >> b) & 1);
-        peers &= ((key >> b) & 1) ? msk : ~msk;
+      if (e < E) {
+        s_off[e] = ex & 0xFFFF;
+        const int c = v4[j] & 0xFFFF;
+        if (c) {
+          const int u = ex >> 16;
+          s_touched[u] = e;
+          for (int k = 0; k < n4[j]; ++k) s_vg[nex + k] = (u << 16) | ((8 * k) << 8) | min(8, c - 8 * k);
+        }
       }
-      const int rank = __popcll(peers & lt);
-      const int cnt = __popcll(peers);
-      if (valid) s_list[s_cur[key] + rank] = q;
-      __builtin_amdgcn_wave_barrier();
-      if (valid && rank == cnt - 1) s_cur[key] += cnt;
-      __builtin_amdgcn_wave_barrier();
+      ex += v4[j];
+      nex += n4[j];
     }
-    // Touched experts, ascending.
-    int nt = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + lane;
-      const bool hit = e < E && s_cnt[e] > 0;
-      const unsigned long long msk = __ballot(hit);
-      if (hit) s_touched[nt + __popcll(msk & lt)] = e;
-      nt += __popcll(msk);
-    }
-    if (lane == 0) s_ntouched = nt;
+    if (lane == 63) { s_off[E] = incl & 0xFFFF; s_U = incl >> 16; s_NV = nincl; }
+  }
+  __syncthreads();
+  for (int q = tid; q < TK; q += kThreads) {
+    const int e = s_tidx[q], t = q / K;
+    s_list[s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u))] = q;
   }
   __syncthreads();
 
   if (a.route_only) {
-    if (blockIdx.x == 0) {
+    if (wg == 0) {
       for (int e = tid; e <= E; e += kThreads) a.offsets_out[e] = s_off[e];
       for (int q = tid; q < TK; q += kThreads) {
         a.perm_out[q] = s_list[q];
@@ -475,152 +458,223 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
     return;
   }
-  const int U = s_ntouched;
-  const int ng = U + 1;   // touched experts, then the shared expert (group index U)
+  const int U = s_U;
 
-  // Down tiles of this workgroup: rows [8 * tile, 8 * tile + 8).  The inner
-  // dimension is split over the waves (wave w takes the contiguous k-steps
-  // [4w, 4w + 4)); routed experts are taken in batches of kDownGroups with
-  // all of a batch's loads in flight together.  The shared expert's rows and
-  // the first routed batch's rows are loaded now, before phase B, so that
-  // their latency overlaps it (they do not depend on h).
-  // Rows >= 8 of the tile repeat row 7, experts past the list repeat the last
-  // one and k-steps past the inner size repeat the last one; those outputs
-  // are ignored or their MFMAs skipped.
-  const int ntiles = (H + kDownRows - 1) / kDownRows;
-  auto koff = [&](int s4, int nk) { return 32 * min(kDownKSteps * wave + s4, nk - 1) + kq; };
-  auto down_rows = [&](int tile, int gb, u32x4 (*ad)[kDownKSteps]) {
-    const int r = min(kDownRows * tile + min(m, kDownRows - 1), H - 1);
+  const int NV = s_NV;
+
+  // Phase C geometry (its first weights are requested during phase B).
+  // Workgroup wg owns output rows [row0, row0 + nrows), nrows <= 8.  A tile
+  // holds two independent 8-row halves: tile rows 8h + r are output row r of
+  // half h, tile columns 8h + p are pair p of half h, and only the two
+  // diagonal 8 x 8 blocks of the product are used.  Stage 0 is the shared
+  // expert (columns: tokens 0-7 and 8-15; h_sh already carries the gate);
+  // stage s >= 1 holds routed chunks 2 (s - 1) and 2 (s - 1) + 1 (columns: the
+  // chunk's pairs; h already weighted).  Wave w takes k-steps [4w, 4w + 4) of
+  // the inner dimension.
+  const int rpw = (H + G - 1) / G;
+  const int row0 = wg * rpw, nrows = max(0, min(rpw, H - row0));
+  const int NS = 1 + (NV + 1) / 2;
+  const int hm = m >> 3, pm = m & 7;     // this lane's A-row / B-column half and index in it
+  const int crow = min(row0 + min(pm, max(nrows, 1) - 1), H - 1);
+  u32x4 ca[kCDepth][kMaxISteps], cb[kCDepth][kMaxISteps];
+  const rsrc_t r_dn = make_rsrc(L.down_w, (size_t)E * H * I * 2);
+  const rsrc_t r_sdn = make_rsrc(L.sh_down_w, (size_t)H * Is * 2);
+  // Column p of half h of stage s: its token and its h row (or -1).
+  auto column = [&](int s, int h, int p, int* tok) -> int {
+    if (s == 0) {
+      const int t = 8 * h + p;
+      *tok = t;
+      return t < T ? t : -1;
+    }
+    const int j = 2 * (s - 1) + h;
+    if (s >= NS || j >= NV) return -1;
+    const int v = s_vg[j];
+    if (p >= (v & 0xFF)) return -1;
+    const int q = s_list[s_off[s_touched[v >> 16]] + ((v >> 8) & 0xFF) + p];
+    *tok = q / K;
+    return q;
+  };
+  // This lane's column of the first stages (their h loads go out right after
+  // the hand-off).
+  int crow_h[kCDepth], ctok[kCDepth];
 #pragma unroll
-    for (int j = 0; j < kDownGroups; ++j) {
-      const bf16_t* rp = L.down_w + ((size_t)s_touched[min(gb + j, max(U - 1, 0))] * H + r) * I;
+  for (int s = 0; s < kCDepth; ++s) {
+    int tok = 0;
+    crow_h[s] = column(s, hm, pm, &tok);
+    ctok[s] = crow_h[s] >= 0 ? tok : -1;
+  }
+  // Stages past the last one, empty halves and k-steps past the inner size
+  // load zeros from outside the resources.
+  auto issue_a = [&](u32x4 (&st)[kMaxISteps], int s) {
+    const int nk = (s == 0 ? Is : I) / 32;
+    uint32_t off = kOutside;
+    if (nrows > 0) {
+      if (s == 0) {
+        off = 2u * (uint32_t)(crow * Is + kq);
+      } else {
+        const int j = 2 * (s - 1) + hm;
+        if (s < NS && j < NV) off = 2u * (uint32_t)((s_touched[s_vg[j] >> 16] * H + crow) * I + kq);
+      }
+    }
+    const rsrc_t rs = s == 0 ? r_sdn : r_dn;
 #pragma unroll
-      for (int s4 = 0; s4 < kDownKSteps; ++s4) ad[j][s4] = ldw(rp + koff(s4, I / 32));
+    for (int s4 = 0; s4 < kMaxISteps; ++s4) {
+      const int ks = kMaxISteps * wave + s4;
+      st[s4] = ldw_buf(rs, ks < nk ? off + 64u * ks : kOutside);
     }
   };
-  u32x4 ad[kDownGroups][kDownKSteps];
-  u32x4 ash[kDownKSteps];
-  const bool has_tile = (int)blockIdx.x < ntiles;
-  if (has_tile) {
-    const int r = min(kDownRows * (int)blockIdx.x + min(m, kDownRows - 1), H - 1);
-#pragma unroll
-    for (int s4 = 0; s4 < kDownKSteps; ++s4) ash[s4] = ldw(L.sh_down_w + (size_t)r * Is + koff(s4, Is / 32));
-    if (U > 0) down_rows(blockIdx.x, 0, ad);
-  }
 
-  // ---------------- phase B: routed gate/up tasks ----------------
+  // ---------------- phase B: routed gate/up blocks ----------------
+  // Block b = (touched expert u = b / (I/8), inner rows i0 = 8 (b % (I/8)) ..
+  // i0 + 7); workgroup wg takes blocks wg, wg + G, ...  Tile row 4j + i holds
+  // the gate row (i < 2) or the up row (i >= 2) of inner row i0 + 2j + (i & 1),
+  // so a lane's four accumulator rows are (g_a, g_b, u_a, u_b) of two inner rows.
   {
-    const int nib = I / 16;
-    for (int task = blockIdx.x; task < U * nib; task += G) gate_up_task(s_touched[task / nib], 16 * (task % nib), 16);
-  }
-
-  // ---------------- phase C: down projection and combine ----------------
-  // acc[cb]: this wave's partial 16x16 tile (rows: the tile's output rows,
-  // columns: tokens 16 cb .. 16 cb + 15), summed over experts in a fixed order.
-  const int ncb = (T + 15) / 16;
-  const rsrc_t r_h = make_rsrc(a.h, (size_t)TK * I * 2);
-  const rsrc_t r_hsh = make_rsrc(a.h_sh, (size_t)T * Is * 2);
-  const rsrc_t r_gs = make_rsrc(a.gate_s, (size_t)T * 4);
-  for (int tile = blockIdx.x; tile < ntiles; tile += G) {
-    const bool first_tile = tile == (int)blockIdx.x;
-    f32x4 acc[4] = {zf4, zf4, zf4, zf4};
-    // Shared expert first: its h was finished in phase A.
-    if (wave == 0) {
-      see_epoch();
-      wait_until([&] { return ld_cnt(ctl + kCtlH + kLine * E) >= (uint32_t)Is; }, err, 1u);
-    }
-    __syncthreads();
-    if (!first_tile) {
-      const int r = min(kDownRows * tile + min(m, kDownRows - 1), H - 1);
+    const int nbi = I / 8;
+    const int NB = U * nbi;
+    const int nmine = NB > wg ? (NB - wg + G - 1) / G : 0;
+    u32x4 wa[kBDepth][kMaxHSteps];
+    const rsrc_t r_gu = make_rsrc(L.gate_up_w, (size_t)E * 2 * I * H * 2);
+    // Stage loads are issued unconditionally: past the last block, and for
+    // k-steps past H / 4, the offsets fall outside the resource.
+    auto issue = [&](u32x4 (&st)[kMaxHSteps], int i) {
+      uint32_t off = kOutside;
+      if (i < nmine) {
+        const int b = wg + i * G, u = b / nbi, i0 = 8 * (b - u * nbi);
+        const int e = s_touched[u];
+        const int row = e * 2 * I + ((m & 2) ? I : 0) + i0 + 2 * (m >> 2) + (m & 1);
+        off = 2u * (uint32_t)(row * H + kbeg + kq);
+      }
 #pragma unroll
-      for (int s4 = 0; s4 < kDownKSteps; ++s4) ash[s4] = ldw(L.sh_down_w + (size_t)r * Is + koff(s4, Is / 32));
-    }
-    for (int cb = 0; cb < ncb; ++cb) {
-      const int t = 16 * cb + m;
-      const uint32_t row = t < T ? 2u * (uint32_t)(t * Is) : kOutside;
-      u32x4 bf[kDownKSteps];
+      for (int ks = 0; ks < kMaxHSteps; ++ks) st[ks] = ldw_buf(r_gu, ks < nks ? off + 64u * ks : kOutside);
+    };
+    auto compute = [&](u32x4 (&st)[kMaxHSteps], int i) {
+      if (i < nmine) {
+        const int b = wg + i * G, u = b / nbi, i0 = 8 * (b - u * nbi);
+        const int e = s_touched[u], beg = s_off[e], cnt = s_off[e + 1] - beg;
+        const int t = s_list[beg + min(m, cnt - 1)] / K;
+        const bf16_t* xs = s_x + t * kXStride + kbeg + kq;
+        u32x4 xb[kMaxHSteps];
 #pragma unroll
-      for (int s4 = 0; s4 < kDownKSteps; ++s4) bf[s4] = ld_pub16(r_hsh, row + 2u * koff(s4, Is / 32));
-      const float sgt = ld_pub_f(r_gs, t < T ? 4u * t : kOutside);
-      f32x4 d = zf4;
-#pragma unroll
-      for (int s4 = 0; s4 < kDownKSteps; ++s4)
-        if (kDownKSteps * wave + s4 < Is / 32) d = mfma16(ash[s4], bf[s4], d);
-      d *= sgt;
-#pragma unroll
-      for (int c4i = 0; c4i < 4; ++c4i)
-        if (c4i == cb) acc[c4i] += d;
-    }
-    // Routed experts: wave 0 waits until every touched expert's h is
-    // complete (lanes poll different experts); the barrier releases the rest.
-    if (wave == 0) {
-      wait_until([&] {
-        bool ok = true;
-        for (int gi = lane; gi < U; gi += 64) ok = ok && ld_cnt(ctl + kCtlH + kLine * s_touched[gi]) >= (uint32_t)I;
-        return __ballot(!ok) == 0ull;
-      }, err, 1u);
-    }
-    __syncthreads();
-    for (int gb = 0; gb < U; gb += kDownGroups) {
-      if (gb > 0 || !first_tile) down_rows(tile, gb, ad);
-      for (int cb = 0; cb < ncb; ++cb) {
-        // This lane's column is token t.  Stage 1: the pair of (t, expert) for
-        // every expert of the batch; stage 2: all h loads; stage 3: zero the
-        // fragments of tokens without that expert; stage 4: MFMAs.
-        const int t = 16 * cb + m, tc = min(t, T - 1);
-        int hq[kDownGroups];
-#pragma unroll
-        for (int j = 0; j < kDownGroups; ++j) {
-          const int g = s_touched[min(gb + j, U - 1)];
-          int q = -1;
-          for (int k = 0; k < K; ++k) q = s_tidx[tc * K + k] == g ? tc * K + k : q;
-          hq[j] = (t < T && gb + j < U) ? q : -1;
-        }
-        u32x4 bf[kDownGroups][kDownKSteps];
-#pragma unroll
-        for (int j = 0; j < kDownGroups; ++j) {
-          const uint32_t row = hq[j] >= 0 ? 2u * (uint32_t)(hq[j] * I) : kOutside;
-#pragma unroll
-          for (int s4 = 0; s4 < kDownKSteps; ++s4) bf[j][s4] = ld_pub16(r_h, row + 2u * koff(s4, I / 32));
-        }
+        for (int ks = 0; ks < kMaxHSteps; ++ks) xb[ks] = ld_lds16(xs + 32 * min(ks, nks - 1));
         f32x4 d = zf4;
 #pragma unroll
-        for (int j = 0; j < kDownGroups; ++j) {
-          if (gb + j >= U) continue;
-#pragma unroll
-          for (int s4 = 0; s4 < kDownKSteps; ++s4)
-            if (kDownKSteps * wave + s4 < I / 32) d = mfma16(ad[j][s4], bf[j][s4], d);
+        for (int ks = 0; ks < kMaxHSteps; ++ks) d = mfma16(st[ks], xb[ks], d);
+        s_red[i & 1][wave][lane] = d;
+        __syncthreads();
+        if (wave == 0 && m < cnt) {
+          const f32x4 p0 = s_red[i & 1][0][lane], p1 = s_red[i & 1][1][lane];
+          const f32x4 p2 = s_red[i & 1][2][lane], p3 = s_red[i & 1][3][lane];
+          const f32x4 sum = (p0 + p1) + (p2 + p3);
+          const int q = s_list[beg + m];
+          const float w = s_tw[q];
+          const float ha = siluf_(sum[0]) * sum[2] * w, hb = siluf_(sum[1]) * sum[3] * w;
+          st_dev(reinterpret_cast<uint32_t*>(a.h + (size_t)q * I + i0 + 2 * (lane >> 4)), pack_bf16x2(ha, hb));
         }
+      }
+    };
+    static_assert(kBDepth == 2, "the loop below is unrolled for two stages");
+    issue(wa[0], 0);
+    issue(wa[1], 1);
+    // The first down-projection stages do not depend on h: request them now,
+    // behind the first gate/up stages, so that they stream during phase B.
 #pragma unroll
-        for (int c4i = 0; c4i < 4; ++c4i)
-          if (c4i == cb) acc[c4i] += d;
+    for (int s = 0; s < kCDepth; ++s) issue_a(ca[s], s);
+    for (int i = 0; i < nmine; i += 2) {
+      compute(wa[0], i);
+      issue(wa[0], i + 2);
+      compute(wa[1], i + 1);
+      issue(wa[1], i + 3);
+    }
+  }
+
+  // ---------------- h hand-off ----------------
+  // Every wave's stores (h, and h_sh from phase A) are complete, then one
+  // arrival for this workgroup on its XCD's counter; wave 0 waits until every
+  // workgroup has arrived (lane x polls XCD x's counter) and the barrier
+  // releases the other waves.
+  stores_complete();
+  __syncthreads();
+  if (wave == 0) {
+    see_epoch();
+    if (lane == 0)
+      __hip_atomic_fetch_add(ctl + kCtlBarB + kLine * (wg & 7), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int x = lane & 7;
+    const uint32_t need = x < G ? (uint32_t)((G - x + 7) / 8) : 0u;
+    wait_until([&] { return __ballot(ld_cnt(ctl + kCtlBarB + kLine * x) < need) == 0ull; }, err, 1u);
+  }
+  __syncthreads();
+
+  // ---------------- phase C: down projection and combine ----------------
+  // Each wave adds its partial tiles into its own LDS accumulator; the four
+  // are summed at the end.
+  {
+    const rsrc_t r_h = make_rsrc(a.h, (size_t)TK * I * 2);
+    const rsrc_t r_hsh = make_rsrc(a.h_sh, (size_t)T * Is * 2);
+    // h rows (row r of h, or of h_sh in stage 0; r < 0: none) for stage s.
+    auto issue_b = [&](u32x4 (&st)[kMaxISteps], int s, int r) {
+      const int inner = s == 0 ? Is : I, nk = inner / 32;
+      const uint32_t row = r >= 0 ? 2u * (uint32_t)(r * inner) : kOutside;
+      const rsrc_t rs = s == 0 ? r_hsh : r_h;
+#pragma unroll
+      for (int s4 = 0; s4 < kMaxISteps; ++s4) {
+        const int ks = kMaxISteps * wave + s4;
+        st[s4] = ld_after16(rs, ks < nk ? row + 2u * (uint32_t)(32 * ks + kq) : kOutside);
+      }
+    };
+    auto compute = [&](u32x4 (&sa)[kMaxISteps], u32x4 (&sb)[kMaxISteps], int tok, int s) {
+      f32x4 d = zf4;
+#pragma unroll
+      for (int s4 = 0; s4 < kMaxISteps; ++s4) d = mfma16(sa[s4], sb[s4], d);
+      if (s < NS && nrows > 0) {
+        // The lane holds rows 4 (lane >> 4) + i of column m: accumulator half
+        // hl = lane >> 5; only columns of the same half are products (the
+        // lane's own column is then the one it loaded: same half, same pm).
+        const int hl = lane >> 5;
+        const bool use = hl == hm && tok >= 0;
+        // The two halves may hold the same token: half 0 first, then half 1.
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          if (use && hl == pass) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int rr = 4 * ((lane >> 4) & 1) + i;
+              if (rr < nrows) s_acc[wave][rr][tok] += d[i];
+            }
+          }
+        }
+      }
+    };
+    static_assert(kCDepth == 6, "the loop below is unrolled for six stages");
+#pragma unroll
+    for (int s = 0; s < kCDepth; ++s) issue_b(cb[s], s, crow_h[s]);
+    for (int g0 = 0; g0 < NS; g0 += kCDepth) {
+#pragma unroll
+      for (int s = 0; s < kCDepth; ++s) {
+        compute(ca[s], cb[s], ctok[s], g0 + s);
+        const int sn = g0 + s + kCDepth;
+        issue_a(ca[s], sn);
+        int tok = 0;
+        const int r = column(sn, hm, pm, &tok);
+        ctok[s] = r >= 0 ? tok : -1;
+        issue_b(cb[s], sn, r);
       }
     }
-    // Sum the four waves' tiles in a fixed order and write rows < 8 of each column.
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_red[wave][cb][(4 * (lane >> 4) + r) * 16 + m] = acc[cb][r];
     __syncthreads();
-    for (int e = tid; e < ncb * 128; e += kThreads) {
-      const int cb = e >> 7, i = (e >> 4) & 7, c = e & 15;
-      const int idx = i * 16 + c;
-      const int t = 16 * cb + c, r = kDownRows * tile + i;
-      if (t < T && r < H) {
-        const float v = (s_red[0][cb][idx] + s_red[1][cb][idx]) + (s_red[2][cb][idx] + s_red[3][cb][idx]);
-        a.out[(size_t)t * H + r] = (bf16_t)f32_to_bf16(v);
-      }
+    if (tid < nrows * T) {
+      const int rr = tid / T, t = tid - rr * T;
+      const float v = (s_acc[0][rr][t] + s_acc[1][rr][t]) + (s_acc[2][rr][t] + s_acc[3][rr][t]);
+      a.out[(size_t)t * H + row0 + rr] = (bf16_t)f32_to_bf16(v);
     }
-    __syncthreads();
   }
 }
 
 }  // namespace
 
-// Plain launch of at most one workgroup per CU: with the device otherwise idle
-// every workgroup is resident at once.  Should some not be (other kernels
-// occupying CUs), the bounded waits still let every wave finish, and the
-// error word in the workspace reports it.
+// Plain launch of one workgroup per CU: with the device otherwise idle every
+// workgroup is resident at once.  Should some not be (other kernels occupying
+// CUs), the bounded waits still let every wave finish, and the error word in
+// the workspace reports it.
 hipError_t launch_decode(const DecodeArgs& args, int grid, hipStream_t s) {
   hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kThreads), 0, s, args);
   return hipGetLastError();
@@ -632,6 +686,13 @@ int decode_max_grid(int num_cus) {
                                                    0) != hipSuccess)
     return 0;
   return per_cu * num_cus;
+}
+
+bool decode_fits(int H, int E, int Is, int grid) {
+  if (grid < 1) return false;
+  const int rows_a = (E + 1 + grid - 1) / grid + 1 + 2 * ((Is + grid - 1) / grid);
+  const int rows_c = (H + grid - 1) / grid;
+  return rows_a <= 16 && rows_c <= 8;
 }
 
 }  // namespace moe

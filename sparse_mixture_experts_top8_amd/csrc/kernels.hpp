@@ -14,8 +14,9 @@ constexpr int kGemmBNW = 128;   // weight rows per tile: gate_up 64 gate + 64 up
 
 __host__ __device__ inline int router_blocks(int64_t T) { return (int)((T + kRouterTokens - 1) / kRouterTokens); }
 
-// Fused decode path (T <= kDecodeMaxT, H <= 2048, I <= 512, Is <= 512).
-constexpr int kDecodeMaxT = 64;
+// Fused decode path (T <= kDecodeMaxT, H <= 2048, I <= 512, Is <= 512, and the
+// per-workgroup row shares of decode_fits).
+constexpr int kDecodeMaxT = 16;
 struct DecodeArgs {
   LayerArgs L;
   const bf16_t* x;      // [T, H]
@@ -23,20 +24,25 @@ struct DecodeArgs {
   int route_only;       // 1: stop after routing and write offsets/perm
   bf16_t* out;          // [T, H]
   uint32_t* ctl;        // control block: epoch, counters, error word
-  float* logits;        // [T, E]
+  uint64_t* logits_t;   // [T, E] tagged logits: fp32 bits in the high word, the call tag in the low word
+  float* logits_out;    // optional [T, E] fp32 logits (route)
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
-  float* gate_s;        // [T]
+  float* gate_s;        // [T] shared-expert gate sigma(x . w_g)
   bf16_t* h;            // [T*K, I] per (token, k) pair, routing weight applied
   bf16_t* h_sh;         // [T, Is]
   int32_t* offsets_out; // route-only: [E + 1]
   int32_t* perm_out;    // route-only: [T*K]
-  unsigned long long epoch;
+  unsigned long long epoch;   // call-unique; its low 32 bits (never 0) tag this call's logits
 };
-constexpr int kDecodeCtlWords = 4 * 32 + 32 * 257;  // one 128-byte line per counter
+constexpr int kDecodeCtlWords = 18 * 32;  // epoch, error word, 16 counters: one 128-byte line each
 
 hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s);
 int decode_max_grid(int num_cus);
+// True when a grid of `grid` workgroups can hold the layer's per-workgroup
+// shares of router rows, the shared gate row, shared gate/up rows and output
+// rows (16-row tiles).
+bool decode_fits(int H, int E, int Is, int grid);
 
 hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
                          float* logits_out, hipStream_t s);

@@ -83,18 +83,21 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   return c;
 }
 
-// The fused decode path serves small batches of the supported shapes; above
-// kDecodePathMaxT tokens the grouped-GEMM path is faster (the fused kernel
-// handles up to kDecodeMaxT and is exercised there by its own limit).
-constexpr int64_t kDecodePathMaxT = 16;
-bool use_decode(const moe_layer_t* L, int64_t T) {
-  return T >= 1 && T <= kDecodePathMaxT && L->hidden <= 2048 && L->expert_inner <= 512 &&
+// The fused decode path serves small batches of the supported shapes
+// (T <= kDecodeMaxT); whether the device's grid can hold the layer's
+// per-workgroup shares is decided at launch (decode_fits), so the workspace of
+// such a call is sized for either path.
+bool decode_shape(const moe_layer_t* L, int64_t T) {
+  return T >= 1 && T <= moe::kDecodeMaxT && L->hidden <= 2048 && L->expert_inner <= 512 &&
          L->shared_inner <= 512;
+}
+bool use_decode(const moe_layer_t* L, int64_t T, int grid) {
+  return decode_shape(L, T) && moe::decode_fits(L->hidden, L->num_experts, L->shared_inner, grid);
 }
 
 struct DecodeCarve {
   uint32_t* ctl;
-  float* logits;
+  uint64_t* logits_t;
   int32_t* topk_idx;
   float* topk_w;
   float* gate_s;
@@ -114,7 +117,7 @@ DecodeCarve carve_decode(const moe_layer_t* L, int64_t T, char* base) {
   };
   DecodeCarve c{};
   c.ctl = (uint32_t*)take(moe::kDecodeCtlWords * 4);
-  c.logits = (float*)take(t * E * 4);
+  c.logits_t = (uint64_t*)take(t * E * 8);
   c.topk_idx = (int32_t*)take(tk * 4);
   c.topk_w = (float*)take(tk * 4);
   c.gate_s = (float*)take(t * 4);
@@ -125,7 +128,8 @@ DecodeCarve carve_decode(const moe_layer_t* L, int64_t T, char* base) {
 }
 
 size_t workspace_need(const moe_layer_t* L, int64_t T) {
-  return use_decode(L, T) ? carve_decode(L, T, nullptr).bytes : carve(L, T, nullptr).bytes;
+  const size_t grouped = carve(L, T, nullptr).bytes;
+  return decode_shape(L, T) ? std::max(grouped, carve_decode(L, T, nullptr).bytes) : grouped;
 }
 
 // Call-unique epochs for the decode path's start protocol: a per-process
@@ -137,8 +141,9 @@ unsigned long long next_epoch() {
     const unsigned long long t = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
     g_epoch.store((t << 16) ^ ((unsigned long long)getpid() << 44) ^ 0x9E3779B97F4A7C15ull);
   });
+  // The low 32 bits tag the decode path's published logits; 0 is never used.
   unsigned long long e = ++g_epoch;
-  if (e == 0) e = ++g_epoch;
+  while ((uint32_t)e == 0u) e = ++g_epoch;
   return e;
 }
 
@@ -213,7 +218,7 @@ moe::DecodeArgs decode_args(const moe_layer_t* L, const void* x, int64_t T, cons
   a.x = (const bf16_t*)x;
   a.T = (int)T;
   a.ctl = c.ctl;
-  a.logits = c.logits;
+  a.logits_t = c.logits_t;
   a.topk_idx = c.topk_idx;
   a.topk_w = c.topk_w;
   a.gate_s = c.gate_s;
@@ -267,13 +272,13 @@ int moe_route(const moe_layer_t* L, const void* x, int64_t T, int32_t* topk_idx,
     return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T = %lld", ws_bytes, need, (long long)T);
   int cus = 0, dgrid = 0;
   if ((rc = device_check(&cus, &dgrid)) != MOE_OK) return rc;
-  if (use_decode(L, T)) {
+  if (use_decode(L, T, dgrid)) {
     moe::DecodeArgs a = decode_args(L, x, T, carve_decode(L, T, (char*)ws));
     a.route_only = 1;
     a.topk_idx = topk_idx;
     a.topk_w = topk_w;
     if (shared_gate) a.gate_s = shared_gate;
-    if (logits) a.logits = logits;
+    a.logits_out = logits;
     a.offsets_out = offsets;
     a.perm_out = perm;
     return launch_status(moe::launch_decode(a, dgrid, (hipStream_t)stream), "decode (route)");
@@ -303,7 +308,7 @@ int moe_forward_traced(const moe_layer_t* L, const void* x, int64_t T, void* out
     return launch_status(hipEventRecord((hipEvent_t)events[i], s), "hipEventRecord");
   };
   if ((rc = mark(0)) != MOE_OK) return rc;
-  if (use_decode(L, T)) {
+  if (use_decode(L, T, dgrid)) {
     moe::DecodeArgs da = decode_args(L, x, T, carve_decode(L, T, (char*)ws));
     da.out = (bf16_t*)out;
     if ((rc = launch_status(moe::launch_decode(da, dgrid, s), "decode")) != MOE_OK) return rc;

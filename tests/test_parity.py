@@ -129,7 +129,7 @@ def toy():
     return d, bits, moe.MoeLayer.from_bf16_bits(bits, d.H, d.E, d.K, d.I, d.Is, "cuda")
 
 
-@pytest.mark.parametrize("T", [8, 1, 2, 31, 32, 33, 63, 64, 65, 127, 129, 300, 1000])
+@pytest.mark.parametrize("T", [8, 1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 129, 300, 1000])
 def test_toy_parity(toy, T):
     d, bits, layer = toy
     _say(f"case toy T={T}")
@@ -255,6 +255,63 @@ def test_full_decode_small_inputs(full):
         r, out = run_layer(layer, xb)
         gi = check_routing(xb, bits, d, r, f"decode small x T={T}")
         check_output(xb, bits, d, gi, _np(out.float()), np.arange(T), f"decode small x T={T}")
+
+
+def test_full_decode_batches(full):
+    # The fused decode path up to its largest batch (16 tokens), then the
+    # first batch size past it; at 16 tokens also run-to-run bitwise
+    # determinism and bitwise token-permutation equivariance.
+    moe = _moe()
+    d, bits, layer, _, _ = full
+    for T in (2, 7, 16, 17):
+        _say(f"case full decode batch T={T}")
+        xb = mi.make_x(d, T, 7000 + T)
+        r, out = run_layer(layer, xb, want_logits=True)
+        gi = check_routing(xb, bits, d, r, f"decode batch T={T}")
+        check_output(xb, bits, d, gi, _np(out.float()), np.arange(T), f"decode batch T={T}")
+        if T == 16:
+            x = moe.bits_to_device(xb, "cuda")
+            a = moe.forward(x, layer)
+            b = moe.forward(x, layer)
+            p = np.random.default_rng(3).permutation(T)
+            c = moe.forward(moe.bits_to_device(xb[p], "cuda"), layer)
+            torch.cuda.synchronize()
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "not bitwise reproducible"
+            assert torch.equal(c.view(torch.int16).cpu(), a.view(torch.int16).cpu()[p])
+            assert torch.equal(a.view(torch.int16), out.view(torch.int16))
+
+
+def test_full_decode_workspace_reuse(full):
+    # Calls that share a workspace must not see each other's intermediate
+    # values: B after A on one workspace equals B on a fresh one, bit for bit.
+    moe = _moe()
+    d, bits, layer, _, _ = full
+    for T in (1, 16):
+        _say(f"case full decode workspace reuse T={T}")
+        xa = moe.bits_to_device(mi.make_x(d, T, 8100 + T), "cuda")
+        xb = moe.bits_to_device(mi.make_x(d, T, 8200 + T), "cuda")
+        ws = layer.workspace(T)
+        fresh = moe.forward(xb, layer, ws=layer.workspace(T))
+        for _ in range(3):
+            moe.forward(xa, layer, ws=ws)
+            got = moe.forward(xb, layer, ws=ws)
+        torch.cuda.synchronize()
+        assert decode_error_word(ws) == 0
+        assert torch.equal(got.view(torch.int16), fresh.view(torch.int16))
+
+
+def test_full_decode_identical_tokens(full):
+    # Sixteen identical tokens: every touched expert holds all 16 pairs (a full
+    # tile of columns) and all output rows must be identical.
+    d, bits, layer, _, _ = full
+    _say("case full decode identical tokens T=16")
+    xb = np.repeat(mi.make_x(d, 1, 4711), 16, axis=0)
+    r, out = run_layer(layer, xb)
+    gi = check_routing(xb, bits, d, r, "identical 16")
+    assert len(np.unique(gi, axis=0)) == 1
+    o = out.view(torch.int16)
+    assert torch.all(o == o[0:1]).item()
+    check_output(xb[:1], bits, d, gi[:1], _np(out.float())[:1], np.arange(1), "identical 16")
 
 
 def test_full_forced_routing_one_hot_segment(full):
