@@ -83,6 +83,60 @@ __device__ __forceinline__ void wave_argmax(float bv, int bi, float* v_out, int*
   *v_out = m;
 }
 
+__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
+// Top-K of NT tokens by one wave (independent chains, interleaved), from each
+// lane's four logits of experts 4 lane + c: descending logit, ties to the
+// lower expert index (the lowest lane among equal lane bests, the lowest c
+// inside a lane); lane k < K receives the k-th index and its weight, the
+// softmax over the selected logits (equal to the full softmax renormalised).
+// A validity mask (experts < E, not yet taken) keeps every pick distinct even
+// among equal or -inf values; NaN counts as -inf.
+template <int NT>
+__device__ __forceinline__ void topk_select(const float (&lv)[NT][4], int E, int K, int lane, int (&idx_out)[NT],
+                                            float (&w_out)[NT]) {
+  float v[NT][4];
+  uint32_t valid[NT];
+  float vmax[NT], den[NT], mine_v[NT];
+  int mine_i[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    valid[j] = 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[j][c] = lv[j][c] == lv[j][c] ? lv[j][c] : -INFINITY;
+      if (4 * lane + c < E) valid[j] |= 1u << c;
+    }
+    vmax[j] = 0.f;
+    den[j] = 0.f;
+    mine_v[j] = 0.f;
+    mine_i[j] = 0;
+  }
+  for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      float bv = -INFINITY;
+      int bc = -1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (((valid[j] >> c) & 1u) && (bc < 0 || v[j][c] > bv)) { bv = v[j][c]; bc = c; }
+      const float mx = wave_max(bv);
+      const unsigned long long win = __ballot(bc >= 0 && bv == mx);
+      const int wl = (int)__builtin_ctzll(win);
+      const int wc = __builtin_amdgcn_readlane(bc, wl);
+      if (lane == wl) valid[j] &= ~(1u << wc);
+      if (k == 0) vmax[j] = mx;
+      den[j] += __expf(mx - vmax[j]);
+      if (lane == k) { mine_v[j] = mx; mine_i[j] = 4 * wl + wc; }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    idx_out[j] = clamp_expert(mine_i[j], E);
+    w_out[j] = __expf(mine_v[j] - vmax[j]) / den[j];
+  }
+}
+
 // 16-byte global load/store as four dwords.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
@@ -110,11 +164,15 @@ struct Work {
   int32_t* topk_idx;   // [T*K]
   float* topk_w;       // [T*K]
   float* gate_s;       // [T]
+  float* rlog;         // [ksplit, T, router_cols(E)]  router partial sums (column E: shared gate)
   int32_t* blk_counts; // [nblk * E]  router-block histograms, then block bases
   int32_t* offsets;    // [E + 1]
   int32_t* tiles_gu;   // [E + 2]   prefix of gate_up tiles per group (group E = shared)
   int32_t* tiles_dn;   // [E + 2]   prefix of down tiles per group
+  int4* tdesc_gu;      // per gate_up tile: group, first slot, rows, row tile | column tile << 16
+  int4* tdesc_dn;      // per down tile, same
   int32_t* perm;       // [T*K]
+  int32_t* slot_tok;   // [T*K]  token of each slot (perm / K)
   int32_t* slot_of;    // [T*K]
   bf16_t* h;           // [T*K, I]
   bf16_t* h_sh;        // [T, Is]

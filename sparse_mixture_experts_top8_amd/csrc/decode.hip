@@ -74,13 +74,9 @@ constexpr int kCtlError = 1 * kLine;     // nonzero after a timed-out wait
 constexpr int kCtlBarB = 2 * kLine;      // + kLine * x: arrivals at the h hand-off from XCD x
 static_assert(kDecodeCtlWords >= 10 * kLine, "control block too small");
 
-__device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
-
-// Weights are read once per call: non-temporal loads keep them from evicting
-// the small hot data (x, h, counters) from the caches.
-__device__ __forceinline__ u32x4 ldw(const bf16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
+// Weight fragment (plain load: on MI355X the non-temporal hint measured
+// slower for these streams).
+__device__ __forceinline__ u32x4 ldw(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 ld_lds16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -114,12 +110,12 @@ __device__ __forceinline__ float ld_pub_f(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ u32x4 ld_after16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-// Weight fragment through a buffer resource, non-temporal; an offset outside
-// the resource returns zeros without touching memory, so pipeline stages past
-// the end of the work and k-steps past the contraction are issued
-// unconditionally (the load counter then matches in every path) and add zero.
+// Weight fragment through a buffer resource; an offset outside the resource
+// returns zeros without touching memory, so pipeline stages past the end of
+// the work and k-steps past the contraction are issued unconditionally (the
+// load counter then matches in every path) and add zero.
 __device__ __forceinline__ u32x4 ldw_buf(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
 // All of this wave's earlier memory operations have completed (stores at the
@@ -162,58 +158,6 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
             r2 = __builtin_amdgcn_readlane(v, 47);
   return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
-}
-
-// Top-K of NT tokens by one wave (independent chains, interleaved), from each
-// lane's four logits of experts 4 lane + c: descending logit, ties to the
-// lower expert index (the lowest lane among equal lane bests, the lowest c
-// inside a lane); lane k < K receives the k-th index and its weight, the
-// softmax over the selected logits (equal to the full softmax renormalised).
-// A validity mask (experts < E, not yet taken) keeps every pick distinct even
-// among equal or -inf values; NaN counts as -inf.
-template <int NT>
-__device__ __forceinline__ void topk_select(const float (&lv)[NT][4], int E, int K, int lane, int (&idx_out)[NT],
-                                            float (&w_out)[NT]) {
-  float v[NT][4];
-  uint32_t valid[NT];
-  float vmax[NT], den[NT], mine_v[NT];
-  int mine_i[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    valid[j] = 0u;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v[j][c] = lv[j][c] == lv[j][c] ? lv[j][c] : -INFINITY;
-      if (4 * lane + c < E) valid[j] |= 1u << c;
-    }
-    vmax[j] = 0.f;
-    den[j] = 0.f;
-    mine_v[j] = 0.f;
-    mine_i[j] = 0;
-  }
-  for (int k = 0; k < K; ++k) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      float bv = -INFINITY;
-      int bc = -1;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (((valid[j] >> c) & 1u) && (bc < 0 || v[j][c] > bv)) { bv = v[j][c]; bc = c; }
-      const float mx = wave_max(bv);
-      const unsigned long long win = __ballot(bc >= 0 && bv == mx);
-      const int wl = (int)__builtin_ctzll(win);
-      const int wc = __builtin_amdgcn_readlane(bc, wl);
-      if (lane == wl) valid[j] &= ~(1u << wc);
-      if (k == 0) vmax[j] = mx;
-      den[j] += __expf(mx - vmax[j]);
-      if (lane == k) { mine_v[j] = mx; mine_i[j] = 4 * wl + wc; }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    idx_out[j] = clamp_expert(mine_i[j], E);
-    w_out[j] = __expf(mine_v[j] - vmax[j]) / den[j];
-  }
 }
 
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {

@@ -31,36 +31,43 @@ __device__ int block_inclusive_scan(int v, int* wave_tot) {
   return v + add;
 }
 
-// One workgroup: expert counts, segment offsets, per-block bases and the tile
-// prefix sums of both grouped GEMMs (group E is the shared expert, T rows).
+// One workgroup per expert: exclusive prefix of the expert's count over the
+// router blocks (written back in place as each block's base inside the
+// expert's segment) and the expert's total (into offsets[e] for the scan).
+__global__ __launch_bounds__(256) void dispatch_count_kernel(LayerArgs L, int T, Work w) {
+  __shared__ int wave_tot[4];
+  const int e = blockIdx.x, E = L.E;
+  const int nblk = router_blocks(T);
+  const int per = (nblk + 255) / 256;            // blocks per thread, contiguous
+  const int b0 = threadIdx.x * per, b1 = min(nblk, b0 + per);
+  int run = 0;
+  for (int b = b0; b < b1; ++b) run += w.blk_counts[(size_t)b * E + e];
+  const int incl = block_inclusive_scan(run, wave_tot);
+  int base = incl - run;
+  for (int b = b0; b < b1; ++b) {
+    const int c = w.blk_counts[(size_t)b * E + e];
+    w.blk_counts[(size_t)b * E + e] = base;
+    base += c;
+  }
+  if (threadIdx.x == 255) w.offsets[e] = incl;
+}
+
+// One workgroup: segment offsets from the expert totals and the tile prefix
+// sums of both grouped GEMMs (group E is the shared expert, T rows).
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, Work w) {
   __shared__ int wave_tot[4];
-  __shared__ int s_off[257];
   const int e = threadIdx.x;
   const int E = L.E, K = L.K;
-  const int nblk = router_blocks(T);
-  int cnt = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) cnt += w.blk_counts[(size_t)b * E + e];
-  const int incl = block_inclusive_scan(e < E ? cnt : 0, wave_tot);
-  const int off = incl - (e < E ? cnt : 0);
-  if (e < E) {
-    w.offsets[e] = off;
-    s_off[e] = off;
-    int run = off;
-    for (int b = 0; b < nblk; ++b) {
-      int c = w.blk_counts[(size_t)b * E + e];
-      w.blk_counts[(size_t)b * E + e] = run;
-      run += c;
-    }
-  }
+  const int cnt = e < E ? w.offsets[e] : 0;
+  const int incl = block_inclusive_scan(cnt, wave_tot);
+  if (e < E) w.offsets[e] = incl - cnt;
   if (e == 0) w.offsets[E] = T * K;
 
   // Tiles per group: ceil(rows / BM) row tiles x (weight rows / BNW) column tiles.
   int gu = 0, dn = 0;
   if (e < E) {
     int mt = (cnt + kGemmBM - 1) / kGemmBM;
-    gu = mt * (2 * L.I / kGemmBNW);
+    gu = mt * ((2 * L.I + kGemmBNW - 1) / kGemmBNW);
     dn = mt * (L.H / kGemmBNW);
   }
   const int gu_incl = block_inclusive_scan(gu, wave_tot);
@@ -73,8 +80,28 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
     const int mt = (T + kGemmBM - 1) / kGemmBM;
     w.tiles_gu[E] = gu_incl;
     w.tiles_dn[E] = dn_incl;
-    w.tiles_gu[E + 1] = gu_incl + mt * (2 * L.Is / kGemmBNW);
+    w.tiles_gu[E + 1] = gu_incl + mt * ((2 * L.Is + kGemmBNW - 1) / kGemmBNW);
     w.tiles_dn[E + 1] = dn_incl + mt * (L.H / kGemmBNW);
+  }
+}
+
+// One workgroup per group (E: the shared expert): the descriptors of its
+// tiles in both grouped GEMMs, column tile major, row tile minor.
+__global__ __launch_bounds__(256) void dispatch_tiles_kernel(LayerArgs L, int T, Work w) {
+  const int g = blockIdx.x, E = L.E;
+  const bool shared = g == E;
+  const int seg0 = shared ? 0 : w.offsets[g];
+  const int nrows = shared ? T : w.offsets[g + 1] - seg0;
+  const int mt = (nrows + kGemmBM - 1) / kGemmBM;
+  const int ngu = (2 * (shared ? L.Is : L.I) + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
+  const int bgu = w.tiles_gu[g], bdn = w.tiles_dn[g];
+  for (int i = threadIdx.x; i < mt * ngu; i += 256) {
+    const int nt = i / mt, mi = i - nt * mt;
+    w.tdesc_gu[bgu + i] = make_int4(g, seg0, nrows, mi | (nt << 16));
+  }
+  for (int i = threadIdx.x; i < mt * ndn; i += 256) {
+    const int nt = i / mt, mi = i - nt * mt;
+    w.tdesc_dn[bdn + i] = make_int4(g, seg0, nrows, mi | (nt << 16));
   }
 }
 
@@ -91,16 +118,19 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(LayerArgs L, int 
   if (j < n) {
     int rank = 0;
     for (int i = 0; i < j; ++i) rank += (keys[i] == key);
-    const int slot = w.blk_counts[(size_t)blockIdx.x * E + key] + rank;
+    const int slot = w.offsets[key] + w.blk_counts[(size_t)blockIdx.x * E + key] + rank;
     w.perm[slot] = q0 + j;
     w.slot_of[q0 + j] = slot;
+    w.slot_tok[slot] = (q0 + j) / K;
   }
 }
 
 }  // namespace
 
 hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s) {
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.E), dim3(256), 0, s, L, T, w);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, L, T, w);
+  hipLaunchKernelGGL(dispatch_tiles_kernel, dim3(L.E + 1), dim3(256), 0, s, L, T, w);
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(router_blocks(T)), dim3(256), 0, s, L, T, w);
   return hipGetLastError();
 }

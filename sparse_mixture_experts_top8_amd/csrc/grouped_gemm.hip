@@ -1,10 +1,10 @@
-// Grouped expert GEMMs on gfx950 MFMA (v_mfma_f32_32x32x16_bf16), one group
+// Grouped expert GEMMs on gfx950 MFMA (v_mfma_f32_16x16x32_bf16), one group
 // per routed expert plus one for the shared expert (group E, all T tokens).
 //
 //  gate_up:  for the rows of group g (gathered x rows of its tokens)
 //            G = A Wg^T, U = A Wu^T,  h = SiLU(G) * U  -> bf16
-//  down:     Y = h Wd^T, scaled in the epilogue by the routing weight of the
-//            row (shared rows: by sigmoid(x . w_sg)) -> bf16 per row
+//  down:     Y = h Wd^T -> bf16 per row (routing weights and the shared gate
+//            are applied when the rows are combined)
 //
 // Definition: "Qwen3.6-35B-A3B — Architecture Overview", section "MoE FFN: 256
 // Experts" (expert_e(x) = SiLU(x W_gate_e) * (x W_up_e) W_down_e, gate and up
@@ -12,181 +12,261 @@
 // sigmoid(Linear(x, 1))); Linnet model page, Blocks: SparseMoe
 // (gate_up_proj [E, 2I, H], down_proj [E, H, I]) and SwiGlu.
 //
-// Both operands are K-contiguous (activation rows, and weights stored
-// [Out, In]), so every 16-byte load feeds eight MFMA k-elements directly.
-// Tiles: 64 rows x 128 weight rows (gate_up: 64 gate + 64 up columns of the
-// same inner range; down: 128 output columns), 64-deep k steps staged
-// through LDS with the next step prefetched into registers.
+// One workgroup per tile of 128 rows x 128 weight rows; two workgroups share
+// a CU, so one's start-up overlaps the other's streaming.  Wave w owns weight
+// rows 32w .. 32w + 31 of the tile as two 16-column MFMA blocks: for gate_up
+// the gate rows and the up rows of the same 16 inner rows (SiLU(g) * u is
+// formed in registers, both blocks having the same layout), for down 32 output
+// columns.  Each wave covers all 128 rows.
 //
-// Scheduling: a persistent grid whose size is a multiple of 8.  Workgroups are
-// handed to the eight XCDs round-robin, so workgroup i runs on XCD i % 8; the
-// tile list is cut into eight contiguous ranges and XCD x walks range x.
-// Neighbouring tiles share a weight slab (row tiles of one column tile) or an
-// activation block (column tiles of one row tile), and these then meet in the
-// same 4 MB L2.
+// k advances in steps of 64 through a four-deep ring, three steps in flight:
+// the weight fragments of a wave are needed by that wave alone and go straight
+// into registers in MFMA operand layout; the activation tile (gathered x rows
+// or h rows) is shared by the four waves and goes to LDS by the direct-to-LDS
+// loads (global_load_lds_dwordx4).  Within a k-step, lane quarter q (lane / 16)
+// covers k 16q .. 16q + 15, eight per MFMA k-step; activations and weights
+// use the same order, so the products are unchanged and each lane reads 32
+// contiguous bytes of a weight row per step.
+//
+// LDS rows of the activation tile are 128 bytes; the 16-byte chunk c of row r
+// is stored at chunk c ^ (r & 7).  LDS is read with inline ds_read_b128 and the
+// load counter waited for explicitly: the compiler would otherwise drain every
+// outstanding direct-to-LDS load before any LDS access.  For the same reason
+// every load in the loop is issued unconditionally, so the counts the
+// explicit waits rely on are exact (rows past a group repeat its last row,
+// k-steps past the contraction read zeros through the weight resource).
+//
+// Scheduling: workgroups are handed to the eight XCDs round-robin (workgroup i
+// on XCD i % 8); the tile list is cut into eight contiguous ranges and XCD x
+// takes range x in order.  Tiles are ordered (group, column tile, row tile): a
+// group's row tiles of one weight slab, and its column tiles of one activation
+// block, run side by side in one XCD and share them through its L2.
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;     // 64 rows
-constexpr int BNW = kGemmBNW;   // 128 weight rows
+constexpr int BM = kGemmBM;      // 128 rows
+constexpr int BN = kGemmBNW;     // 128 weight rows
 constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements; +16 B breaks the 128 B row period
+constexpr int NS = 4;            // ring depth (activation LDS stages = weight register slots)
+constexpr int kATile = BM * BK * 2;     // 16 KB
+constexpr int kVmPerStep = 4 + 4;       // per wave: 4 direct-to-LDS + 4 weight loads
 
-__device__ __forceinline__ int find_group(const int* __restrict__ prefix, int E, int t) {
-  // Largest g in [0, E] with prefix[g] <= t (prefix is non-decreasing, prefix[0] = 0).
-  int lo = 0, hi = E;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutside = 0x80000000u;
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// Waits for the LDS reads and ties their result registers to the wait, so
+// that no use of them can be scheduled before it.
+__device__ __forceinline__ void wait_lds(u32x4 (&a)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+               :
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
 template <bool GATE_UP>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const bf16_t* __restrict__ x,
-                                                             int T, Work w) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BNW * LDS_STRIDE];
+__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
+                                                             Work w, const int* __restrict__ prefix,
+                                                             const int4* __restrict__ tdesc,
+                                                             const int* __restrict__ slot_tok) {
+  __shared__ __attribute__((aligned(1024))) char lds[NS * kATile];
+
+  const int E = L.E, K = L.K, H = L.H;
+  // Tile of this workgroup: XCD x = blockIdx % 8 takes the x-th contiguous
+  // eighth of the tile list, in order.
+  const int ntiles = uni(prefix[E + 1]);
+  const int chunk = (ntiles + 7) >> 3;
+  const int j8 = blockIdx.x >> 3;
+  if (j8 >= chunk) return;
+  const int t = (blockIdx.x & 7) * chunk + j8;
+  if (t >= ntiles) return;
+  const int4 d = tdesc[t];
+  const int g = uni(d.x), seg0 = uni(d.y), nrows = uni(d.z);
+  const int m0 = uni(d.w & 0xFFFF) * BM, nt = uni(d.w >> 16);
+  const bool shared = g == E;
+  const int kdim = GATE_UP ? H : (shared ? L.Is : L.I);
+  const int inner_n = shared ? L.Is : L.I;           // gate_up: inner rows of the group
+  const int nreal = kdim / BK;                       // real k-steps
+  const int nsteps = ((nreal + NS - 1) / NS) * NS;   // padded to the ring depth (padding: zero weights)
+  const int rows_here = min(BM, nrows - m0);         // rows of this tile inside the group (>= 1)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int E = L.E, K = L.K, H = L.H;
-  const int* __restrict__ prefix = GATE_UP ? w.tiles_gu : w.tiles_dn;
-  const int ntiles = prefix[E + 1];
+  const int wv = uni(wave);
+  const int l16 = lane & 15, q = lane >> 4;
+  const uint32_t lds_base = (uint32_t)(size_t)(lds_ptr_t)lds;
 
-  const int per_xcd = gridDim.x >> 3;
-  const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
-  const int chunk = (ntiles + 7) >> 3;
-  const int t_end = min(ntiles, (xcd + 1) * chunk);
-
-  for (int tile = xcd * chunk + slot_in_xcd; tile < t_end; tile += per_xcd) {
-    const int g = find_group(prefix, E, tile);
-    const bool shared = (g == E);
-    const int seg0 = shared ? 0 : w.offsets[g];
-    const int nrows = shared ? T : (w.offsets[g + 1] - seg0);
-    const int mt = (nrows + BM - 1) / BM;
-    const int local = tile - prefix[g];
-    const int m0 = (local % mt) * BM;
-    const int nt = local / mt;
-    const int inner = shared ? L.Is : L.I;
-    const int kdim = GATE_UP ? H : inner;
-
-    // ---- per-thread source rows: 2 A chunks and 4 B chunks of 16 B per k step ----
-    const bf16_t* a_src[2];
-    bool a_ok[2];
+  // ---- activation sources: direct-to-LDS instruction j (0..3) of wave w
+  // writes 16-byte unit p = 64 (4 j + w) + lane, i.e. row r = 8 (4 j + w) +
+  // lane / 8, stored chunk lane % 8, holding the global chunk (lane % 8) ^ (r & 7).
+  const bf16_t* a_src[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 3, col = (c & 7) * 8;
-      const int row = m0 + r;
-      a_ok[i] = row < nrows;
-      const int rr = a_ok[i] ? row : 0;
-      if (GATE_UP) {
-        const int tok = shared ? rr : (w.perm[seg0 + rr] / K);
-        a_src[i] = x + (size_t)tok * H + col;
-      } else {
-        a_src[i] = shared ? (w.h_sh + (size_t)rr * L.Is + col) : (w.h + (size_t)(seg0 + rr) * L.I + col);
-      }
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * (4 * j + wv) + (lane >> 3);
+    const int gch = ((lane & 7) ^ (r & 7)) * 8;
+    const int row = m0 + min(r, rows_here - 1);         // rows past the group repeat its last row
+    if (GATE_UP) {
+      const int tok = shared ? row : slot_tok[seg0 + row];
+      a_src[j] = x + (size_t)tok * H + gch;
+    } else {
+      a_src[j] = shared ? w.h_sh + (size_t)row * L.Is + gch : w.h + (size_t)(seg0 + row) * L.I + gch;
     }
-    const bf16_t* b_src[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 3, col = (c & 7) * 8;
-      if (GATE_UP) {
-        // r < 64: gate row nt*64 + r; r >= 64: up row nt*64 + r - 64.
-        const int inner_row = nt * 64 + (r & 63);
-        if (shared)
-          b_src[i] = (r < 64 ? L.sh_gate_w : L.sh_up_w) + (size_t)inner_row * H + col;
-        else
-          b_src[i] = L.gate_up_w + ((size_t)g * 2 * L.I + (r < 64 ? 0 : L.I) + inner_row) * H + col;
-      } else {
-        const int n = nt * BNW + r;
-        b_src[i] = shared ? (L.sh_down_w + (size_t)n * L.Is + col)
-                          : (L.down_w + ((size_t)g * H + n) * L.I + col);
-      }
+  }
+  // ---- weight sources: block b (0, 1) of wave w is weight row (of the tile)
+  // 32 w + 16 b + lane % 16; lane quarter q reads elements 16q .. 16q + 15 of
+  // each k-step (two 16-byte loads), through a buffer resource.
+  rsrc_t b_rs[2];
+  uint32_t b_off[2];
+  if (GATE_UP) {
+    const int inner = min(nt * 64 + 16 * wv + l16, inner_n - 1);   // past the inner size: repeated, dropped
+    if (shared) {
+      b_rs[0] = make_rsrc(L.sh_gate_w, (uint32_t)(L.Is * H * 2));
+      b_rs[1] = make_rsrc(L.sh_up_w, (uint32_t)(L.Is * H * 2));
+      b_off[0] = b_off[1] = 2u * (uint32_t)(inner * H + 16 * q);
+    } else {
+      b_rs[0] = b_rs[1] = make_rsrc(L.gate_up_w + (size_t)g * 2 * L.I * H, (uint32_t)(2 * L.I * H * 2));
+      b_off[0] = 2u * (uint32_t)(inner * H + 16 * q);
+      b_off[1] = 2u * (uint32_t)((L.I + inner) * H + 16 * q);
     }
-
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-    u32x4 ra[2], rb[4];
+  } else {
+    const bf16_t* base = shared ? L.sh_down_w : L.down_w + (size_t)g * H * L.I;
+    b_rs[0] = b_rs[1] = make_rsrc(base, (uint32_t)(H * kdim * 2));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ra[i] = a_ok[i] ? ld16(a_src[i]) : zero4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rb[i] = ld16(b_src[i]);
+    for (int b = 0; b < 2; ++b) b_off[b] = 2u * (uint32_t)((nt * BN + 32 * wv + 16 * b + l16) * kdim + 16 * q);
+  }
 
-    f32x16 acc0, acc1;
+  u32x4 wb[NS][2][2];     // weight fragments: [slot][block][k-step of 32]
+  auto issue = [&](u32x4 (&wbs)[2][2], int st, int ks) {
+    char* sbase = lds + st * kATile;
+    const int kv = min(ks, nreal - 1);          // padding steps re-read the last real step
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; }
-
-    // MFMA operand rows of this wave inside the tile.
-    const int a_row = 32 * wm + (lane & 31);
-    const int b_row0 = GATE_UP ? (32 * wn + (lane & 31)) : (64 * wn + (lane & 31));
-    const int b_row1 = GATE_UP ? (64 + 32 * wn + (lane & 31)) : (64 * wn + 32 + (lane & 31));
-    const int kofs = 8 * (lane >> 5);
-
-    for (int k0 = 0; k0 < kdim; k0 += BK) {
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + kv * BK), (lds_ptr_t)(sbase + 1024 * (4 * j + wv)),
+                                       16, 0, 0);
+    const bool real = ks < nreal;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i;
-        *reinterpret_cast<u32x4*>(&As[(c >> 3) * LDS_STRIDE + (c & 7) * 8]) = ra[i];
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        wbs[b][h] = __builtin_amdgcn_raw_buffer_load_b128(
+            b_rs[b], real ? b_off[b] + 2u * (uint32_t)(ks * BK + 8 * h) : kOutside, 0, 0);
+  };
+
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[i][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int mblocks = (rows_here + 15) >> 4;    // 16-row blocks holding rows of the group
+
+  issue(wb[0], 0, 0);
+  issue(wb[1], 1, 1);
+  issue(wb[2], 2, 2);
+  auto step = [&](u32x4 (&wcur)[2][2], u32x4 (&wnext)[2][2], int st, int ks) {
+    // This step's loads must have landed; younger are the loads of the later
+    // steps already issued (at most two), 8 per step and wave.
+    const int younger = min(2, nsteps - 1 - ks);
+    if (younger == 2) wait_vm<2 * kVmPerStep>();
+    else if (younger == 1) wait_vm<kVmPerStep>();
+    else wait_vm<0>();
+    barrier();   // every wave's part of the stage is in LDS; the stage read last step is free
+    if (ks + 3 < nsteps) issue(wnext, (st + 3) % NS, ks + 3);
+    const uint32_t sa = lds_base + st * kATile;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 av[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ra = 16 * i + l16;
+        av[i] = lds_read16(sa + ra * 128 + (((2 * q + h) ^ (ra & 7)) << 4));
       }
+      wait_lds(av);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        *reinterpret_cast<u32x4*>(&Bs[(c >> 3) * LDS_STRIDE + (c & 7) * 8]) = rb[i];
-      }
-      __syncthreads();
-      if (k0 + BK < kdim) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) ra[i] = a_ok[i] ? ld16(a_src[i] + k0 + BK) : zero4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rb[i] = ld16(b_src[i] + k0 + BK);
-      }
-#pragma unroll
-      for (int kk = 0; kk < BK; kk += 16) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&As[a_row * LDS_STRIDE + kk + kofs]));
-        const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Bs[b_row0 * LDS_STRIDE + kk + kofs]));
-        const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Bs[b_row1 * LDS_STRIDE + kk + kofs]));
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
-      }
-      __syncthreads();
-    }
-
-    // ---- epilogue: D[8*(r/4) + 4*(lane/32) + r%4][lane%32] ----
-    const int col = lane & 31;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= nrows) continue;
-      if (GATE_UP) {
-        const float hv = siluf_(acc0[r]) * acc1[r];
-        const int icol = nt * 64 + 32 * wn + col;
-        bf16_t* dst = shared ? (w.h_sh + (size_t)row * L.Is) : (w.h + (size_t)(seg0 + row) * L.I);
-        dst[icol] = (bf16_t)f32_to_bf16(hv);
-      } else {
-        float scale;
-        size_t yrow;
-        if (shared) {
-          scale = w.gate_s[row];
-          yrow = (size_t)T * K + row;
-        } else {
-          scale = w.topk_w[w.perm[seg0 + row]];
-          yrow = (size_t)(seg0 + row);
+      for (int i = 0; i < 8; ++i) {
+        if (i < mblocks) {
+          acc[i][0] = mfma16(av[i], wcur[0][h], acc[i][0]);
+          acc[i][1] = mfma16(av[i], wcur[1][h], acc[i][1]);
         }
-        bf16_t* dst = w.y + yrow * H + nt * BNW + 64 * wn + col;
-        dst[0] = (bf16_t)f32_to_bf16(scale * acc0[r]);
-        dst[32] = (bf16_t)f32_to_bf16(scale * acc1[r]);
       }
     }
+  };
+  static_assert(NS == 4, "the loop below is unrolled for four slots");
+  for (int k4 = 0; k4 < nsteps; k4 += NS) {
+    step(wb[0], wb[3], 0, k4);
+    step(wb[1], wb[0], 1, k4 + 1);
+    step(wb[2], wb[1], 2, k4 + 2);
+    step(wb[3], wb[2], 3, k4 + 3);
+  }
+
+  // ---- epilogue: D[4 (lane / 16) + i][lane % 16] of each 16 x 16 block ----
+  // All loads have landed (the last step waited for zero outstanding); every
+  // wave has passed the last step's barrier only after the others finished
+  // reading the stage before it, so a barrier here frees the whole LDS.
+  // Each wave writes its part as bf16 into its own LDS tile (row-major), then
+  // stores 16-byte row chunks; rows past the group fall outside the store
+  // resource and are dropped.
+  barrier();
+  bf16_t* ep = reinterpret_cast<bf16_t*>(lds + wv * (BM * 32 * 2));    // 128 rows x 32 columns (8 KB) per wave
+  constexpr int kCols = GATE_UP ? 16 : 32;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int b = 0; b < (GATE_UP ? 1 : 2); ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = GATE_UP ? siluf_(acc[i][0][r]) * acc[i][1][r] : acc[i][b][r];
+        ep[(16 * i + 4 * q + r) * kCols + 16 * b + l16] = (bf16_t)f32_to_bf16(v);
+      }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  bf16_t* obase;
+  uint32_t ostride, ocol;
+  bool wave_ok = true;
+  if (GATE_UP) {
+    ocol = nt * 64 + 16 * wv;
+    wave_ok = (int)ocol < inner_n;
+    ostride = inner_n * 2;
+    obase = (shared ? w.h_sh : w.h) + (size_t)(seg0 + m0) * inner_n;
+  } else {
+    ocol = nt * BN + 32 * wv;
+    ostride = H * 2;
+    obase = w.y + ((shared ? (size_t)T * K : (size_t)seg0) + m0) * H;
+  }
+  const rsrc_t ors = make_rsrc(obase, wave_ok ? (uint32_t)rows_here * ostride : 0u);
+  constexpr int kChunks = kCols / 8;                 // 16-byte chunks per row
+#pragma unroll
+  for (int c0 = 0; c0 < BM * kChunks; c0 += 64) {
+    const int c = c0 + lane, row = c / kChunks, cc = c % kChunks;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ep + row * kCols + 8 * cc);
+    __builtin_amdgcn_raw_buffer_store_b128(v, ors, (uint32_t)row * ostride + 2u * ocol + 16u * cc, 0, 0);
   }
 }
 
-// out[t] = bf16( sum_k y[slot_of(t, k)] + y[T*K + t] ), k in order, fp32 sum.
+// out[t] = bf16( sum_k w[t, k] y[slot_of(t, k)] + gate[t] y[T*K + t] ), k in
+// order, fp32 sum.
 __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int K, Work w, bf16_t* __restrict__ out) {
   const int per_tok = H >> 3;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -197,11 +277,12 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int K, Work 
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   for (int k = 0; k <= K; ++k) {
     const size_t row = k < K ? (size_t)w.slot_of[(size_t)t * K + k] : (size_t)T * K + t;
+    const float sc = k < K ? w.topk_w[(size_t)t * K + k] : w.gate_s[t];
     const u32x4 v = ld16(w.y + row * H + c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += bf16_to_f32(v[j] & 0xFFFFu);
-      acc[2 * j + 1] += bf16_to_f32(v[j] >> 16);
+      acc[2 * j] += sc * bf16_to_f32(v[j] & 0xFFFFu);
+      acc[2 * j + 1] += sc * bf16_to_f32(v[j] >> 16);
     }
   }
   u32x4 o;
@@ -210,22 +291,27 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int K, Work 
   st16(out + (size_t)t * H + c, o);
 }
 
-int persistent_grid(int num_cus) {
-  int g = num_cus * 2;
-  return ((g + 7) / 8) * 8;
-}
+unsigned gemm_grid(int64_t bound) { return (unsigned)(8 * ((bound + 7) / 8)); }
 
 }  // namespace
 
 hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work& w, int num_cus,
                           hipStream_t s) {
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(persistent_grid(num_cus)), dim3(256), 0, s, L, x, T, w);
+  (void)num_cus;
+  // The dispatch tables go in as separate read-only arguments: uniform reads of
+  // them then compile to scalar loads.
+  const int64_t bound = gemm_tile_bound(T, L.K, L.E, 2 * L.I, 2 * L.Is);
+  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(gemm_grid(bound)), dim3(256), 0, s, L, x, T, w,
+                     (const int*)w.tiles_gu, (const int4*)w.tdesc_gu, (const int*)w.slot_tok);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s) {
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(persistent_grid(num_cus)), dim3(256), 0, s, L,
-                     (const bf16_t*)nullptr, T, w);
+  (void)num_cus;
+  const int64_t bound = gemm_tile_bound(T, L.K, L.E, L.H, L.H);
+  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(gemm_grid(bound)), dim3(256), 0, s, L,
+                     (const bf16_t*)nullptr, T, w, (const int*)w.tiles_dn, (const int4*)w.tdesc_dn,
+                     (const int*)w.slot_tok);
   return hipGetLastError();
 }
 

@@ -9,10 +9,21 @@ namespace moe {
 // Router tile: tokens per router workgroup (also the dispatch block size).
 constexpr int kRouterTokens = 32;
 // Grouped-GEMM tile: rows (slots) per tile, weight rows per tile.
-constexpr int kGemmBM = 64;
+constexpr int kGemmBM = 128;
 constexpr int kGemmBNW = 128;   // weight rows per tile: gate_up 64 gate + 64 up; down 128 H cols
+// Upper bound of the tiles of one grouped GEMM (workspace and grid size):
+// every group adds at most one partial row tile.
+__host__ __device__ inline int64_t gemm_tile_bound(int64_t T, int K, int E, int wrows, int wrows_shared) {
+  const int64_t nt = (wrows + kGemmBNW - 1) / kGemmBNW, nts = (wrows_shared + kGemmBNW - 1) / kGemmBNW;
+  return ((T * K + kGemmBM - 1) / kGemmBM + E) * nt + ((T + kGemmBM - 1) / kGemmBM) * nts;
+}
 
 __host__ __device__ inline int router_blocks(int64_t T) { return (int)((T + kRouterTokens - 1) / kRouterTokens); }
+// Columns of a row of router partial sums: E logits, the shared gate, padding
+// to a multiple of 4.
+__host__ __device__ inline int router_cols(int E) { return (E + 1 + 3) & ~3; }
+// Slices of H the router's logits GEMM is split into for T tokens.
+int router_ksplit(int T, int H);
 
 // Fused decode path (T <= kDecodeMaxT, H <= 2048, I <= 512, Is <= 512, and the
 // per-workgroup row shares of decode_fits).

@@ -70,12 +70,16 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   c.w.topk_idx = (int32_t*)take(tk * 4);
   c.w.topk_w = (float*)take(tk * 4);
   c.w.gate_s = (float*)take(t * 4);
+  c.w.rlog = (float*)take((size_t)moe::router_ksplit((int)T, (int)H) * t * moe::router_cols((int)E) * 4);
   c.w.blk_counts = (int32_t*)take(nblk * E * 4);
   c.w.offsets = (int32_t*)take((E + 1) * 4);
   c.w.tiles_gu = (int32_t*)take((E + 2) * 4);
   c.w.tiles_dn = (int32_t*)take((E + 2) * 4);
+  c.w.tdesc_gu = (int4*)take((size_t)moe::gemm_tile_bound(T, (int)K, (int)E, 2 * (int)I, 2 * (int)Is) * 16);
+  c.w.tdesc_dn = (int4*)take((size_t)moe::gemm_tile_bound(T, (int)K, (int)E, (int)H, (int)H) * 16);
   c.w.perm = (int32_t*)take(tk * 4);
   c.w.slot_of = (int32_t*)take(tk * 4);
+  c.w.slot_tok = (int32_t*)take(tk * 4);
   c.w.h = (bf16_t*)take(tk * I * 2);
   c.w.h_sh = (bf16_t*)take(t * Is * 2);
   c.w.y = (bf16_t*)take((tk + t) * H * 2);

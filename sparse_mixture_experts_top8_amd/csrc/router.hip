@@ -1,8 +1,8 @@
-// Router of the MoE layer on gfx950: logits = x W_r^T with bf16 MFMA, then per
-// token a wavefront-level top-K (descending logit, ties to the lower expert
-// index), the softmax renormalised over the selected experts, the shared-expert
-// gate scalar sigmoid(x . w_sg), and a per-block expert histogram that the
-// dispatch step turns into segment offsets.
+// Router of the MoE layer on gfx950 (grouped path): logits = x W_r^T with bf16
+// MFMA, then per token the top-K (descending logit, ties to the lower expert
+// index), the softmax renormalised over the selected experts, the
+// shared-expert gate scalar sigmoid(x . w_sg), and a per-block expert
+// histogram that the dispatch step turns into segment offsets.
 //
 // Definition: "Qwen3.6-35B-A3B — Architecture Overview", section "MoE FFN: 256
 // Experts" (router Linear 2048 -> 256, softmax, top-8, renormalise to sum 1;
@@ -12,177 +12,174 @@
 // Softmax over all experts followed by renormalisation over the K selected is
 // the same quantity as a softmax over the K selected logits alone (the full
 // denominator cancels); the kernel computes the latter.
+//
+// Two kernels.  router_logits_kernel: one workgroup per (32-token tile, slice
+// of H); the shared gate row rides along as column E, so the E + 1 columns
+// are 17 MFMA column blocks of 16.  Each wave streams its column blocks' rows
+// and the tile's x rows through a four-step register pipeline and writes fp32
+// partial sums.  Small batches split H into up to H/64 slices so that the
+// launch still spans the chip (a 64-token batch would otherwise be two
+// workgroups each reading the whole router).  router_select_kernel: one
+// workgroup per 32 tokens sums the slices in a fixed order and selects.
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kTok = kRouterTokens;      // 32 tokens per workgroup
-constexpr int kLdsStride = 256 + 4;      // padded logits row (E <= 256)
+constexpr int kTok = kRouterTokens;      // 32 tokens per tile
+constexpr int kColBlocks = 5;            // column blocks per wave (17 for E = 256, plus the gate column)
+constexpr int kDepth = 4;                // k-steps in flight per wave
+constexpr int kMaxRouterCols = 260;      // router_cols(256)
 
-// Logits accumulate in fp32 MFMA accumulators; every 256 elements of H the
-// partial sums are folded into a second fp32 total, which keeps the rounding
-// error of the long dot product near that of a pairwise sum.
-__global__ __launch_bounds__(256) void router_topk_kernel(LayerArgs L, const bf16_t* __restrict__ x,
-                                                         int T, Work w, float* __restrict__ logits_out) {
-  __shared__ float lg[kTok * kLdsStride];
-  __shared__ int hist[256];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * kTok;
-  const int H = L.H, E = L.E, K = L.K;
-  hist[tid] = 0;
-
-  // ---- logits tile [32 tokens x E] with v_mfma_f32_16x16x32_bf16 ----
-  // Lane l supplies row (l % 16) and k-group 8*(l / 16) of both operands;
-  // the result lands as D[4*(l/16) + r][l % 16].
-  const int nsub_e = (E + 15) >> 4;
+__global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
+                                                            int ksplit, float* __restrict__ part) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * kTok, s = blockIdx.y;
+  const int H = L.H, E = L.E, Ep = router_cols(E);
+  const int nsub = (E + 1 + 15) >> 4;               // column blocks incl. the gate column
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int klen = H / ksplit, kbeg = s * klen, nk = klen / 32;
+
+  // Operand rows of this lane: x rows of the two 16-token halves, weight rows
+  // of the wave's column blocks (rows past T or E + 1 repeat a valid row and
+  // their outputs are dropped).
   const bf16_t* arow[2];
-  bool aval[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int t = t0 + 16 * i + r16;
-    aval[i] = t < T;
-    arow[i] = x + (size_t)(aval[i] ? t : 0) * H + kq;
-  }
-  const bf16_t* brow[4];
-  bool bval[4];
+  for (int i = 0; i < 2; ++i) arow[i] = x + (size_t)min(t0 + 16 * i + r16, T - 1) * H + kbeg + kq;
+  const bf16_t* brow[kColBlocks];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    int j = wave + 4 * jj;
-    int e = 16 * j + r16;
-    bval[jj] = (j < nsub_e) && (e < E);
-    brow[jj] = L.router_w + (size_t)(bval[jj] ? e : 0) * H + kq;
+  for (int jj = 0; jj < kColBlocks; ++jj) {
+    const int e = min(16 * (wave + 4 * jj) + r16, E);
+    brow[jj] = (e < E ? L.router_w + (size_t)e * H : L.sh_expert_gate) + kbeg + kq;
   }
-  f32x4 acc[2][4], tot[2][4];
+  f32x4 acc[2][kColBlocks], tot[2][kColBlocks];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < kColBlocks; ++jj) {
       acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
       tot[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    u32x4 a[2], b[4];
+  // Ring of kDepth k-steps; loads of k-steps past the slice repeat its last
+  // step (always in bounds) and are not used.
+  u32x4 ra[kDepth][2], rb[kDepth][kColBlocks];
+  auto issue = [&](int st, int ks) {
+    const int k = 32 * min(ks, nk - 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = aval[i] ? ld16(arow[i] + k0) : zero4;
+    for (int i = 0; i < 2; ++i) ra[st][i] = ld16(arow[i] + k);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) b[jj] = bval[jj] ? ld16(brow[jj] + k0) : zero4;
+    for (int jj = 0; jj < kColBlocks; ++jj) rb[st][jj] = ld16(brow[jj] + k);
+  };
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      if (wave + 4 * jj < nsub_e) {
+  for (int st = 0; st < kDepth; ++st) issue(st, st);
+  for (int k0 = 0; k0 < nk; k0 += kDepth) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i]), as_bf16x8(b[jj]),
-                                                               acc[i][jj], 0, 0, 0);
+    for (int st = 0; st < kDepth; ++st) {
+      const int ks = k0 + st;
+      if (ks < nk) {
+#pragma unroll
+        for (int jj = 0; jj < kColBlocks; ++jj) {
+          if (wave + 4 * jj < nsub) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[st][i]), as_bf16x8(rb[st][jj]),
+                                                                   acc[i][jj], 0, 0, 0);
+          }
+        }
+        // Every 256 elements the running sums fold into a second fp32 total,
+        // which keeps the rounding error of the long dot product near that of
+        // a pairwise sum.
+        if ((ks & 7) == 7 || ks == nk - 1) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jj = 0; jj < kColBlocks; ++jj) {
+              tot[i][jj] += acc[i][jj];
+              acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
       }
+      issue(st, ks + kDepth);
     }
-    if (((k0 + 32) & 255) == 0) {
+  }
+  // D[4 (lane / 16) + r][lane % 16] of each 16 x 16 block.
+  float* out = part + (size_t)s * T * Ep;
+#pragma unroll
+  for (int jj = 0; jj < kColBlocks; ++jj) {
+    const int e = 16 * (wave + 4 * jj) + r16;
+    if (wave + 4 * jj < nsub && e <= E) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          tot[i][jj] += acc[i][jj];
-          acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 16 * i + 4 * (lane >> 4) + r;
+          if (t < T) out[(size_t)t * Ep + e] = tot[i][jj][r];
         }
     }
   }
+}
+
+// One workgroup per 32 tokens.  First all threads sum the slices of the
+// tile's partial rows in a fixed order (eight slices' loads in flight at a
+// time) into LDS; then each wave selects for eight tokens, in two interleaved
+// groups of four: top-K, weights, gate, block histogram.
+__global__ __launch_bounds__(256) void router_select_kernel(LayerArgs L, int T, int ksplit,
+                                                            const float* __restrict__ part, Work w,
+                                                            float* __restrict__ logits_out) {
+  __shared__ __attribute__((aligned(16))) float s_lg[kTok][kMaxRouterCols];
+  __shared__ int hist[256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int E = L.E, K = L.K, Ep = router_cols(E), c4n = Ep / 4;
+  const int t0 = blockIdx.x * kTok;
+  hist[tid] = 0;
+  for (int idx = tid; idx < kTok * c4n; idx += 256) {
+    const int tl = idx / c4n, c4 = idx - tl * c4n;
+    const float* src = part + (size_t)min(t0 + tl, T - 1) * Ep + 4 * c4;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ksplit; s0 += 8) {
+      u32x4 q[8];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    int j = wave + 4 * jj;
-    int e = 16 * j + r16;
-    if (j < nsub_e && e < E) {
+      for (int i = 0; i < 8; ++i) q[i] = ld16(src + (size_t)min(s0 + i, ksplit - 1) * T * Ep);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < ksplit)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lg[(16 * i + 4 * (lane >> 4) + r) * kLdsStride + e] = tot[i][jj][r];
+          for (int c = 0; c < 4; ++c) v[c] += __uint_as_float(q[i][c]);
     }
+    *reinterpret_cast<f32x4*>(&s_lg[tl][4 * c4]) = v;
   }
   __syncthreads();
-
-  // ---- per token: top-K, renormalised weights, shared gate, histogram ----
-  for (int tl = wave; tl < kTok; tl += 4) {
-    const int t = t0 + tl;
-    if (t >= T) break;
-    float v[4];
+  for (int g = 0; g < 2; ++g) {
+    float lv[4][4];
+    int tt[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      int e = lane + 64 * c;
-      v[c] = e < E ? lg[tl * kLdsStride + e] : -INFINITY;
-      if (v[c] != v[c]) v[c] = -INFINITY;  // NaN never outranks a number
-    }
-    if (logits_out) {
+    for (int j = 0; j < 4; ++j) {
+      const int tl = wave * 8 + g * 4 + j;
+      tt[j] = t0 + tl;
+      // Columns 4 lane .. 4 lane + 3; past E they are outside the top-K's
+      // valid range (reads stay inside the padded row).
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        int e = lane + 64 * c;
-        if (e < E) logits_out[(size_t)t * E + e] = lg[tl * kLdsStride + e];
+      for (int c = 0; c < 4; ++c) lv[j][c] = s_lg[tl][min(4 * lane + c, kMaxRouterCols - 1)];
+      if (tt[j] < T && lane == 0) w.gate_s[tt[j]] = sigmoidf_(s_lg[tl][E]);
+      if (logits_out && tt[j] < T) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (4 * lane + c < E) logits_out[(size_t)tt[j] * E + 4 * lane + c] = lv[j][c];
       }
     }
-    float sel_v[8];
-    int sel_i[8];
+    int ix[4];
+    float wv[4];
+    topk_select<4>(lv, E, K, lane, ix, wv);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      sel_v[k] = 0.f;
-      sel_i[k] = 0;
-      if (k < K) {
-        // Best candidate of this lane: lowest column wins ties (strict >).
-        // Padding columns (e >= E) hold -inf and lose every tie to a real
-        // expert, so the selected index is always below E.
-        float bv = v[0];
-        int bi = lane;
-#pragma unroll
-        for (int c = 1; c < 4; ++c)
-          if (v[c] > bv) { bv = v[c]; bi = lane + 64 * c; }
-        // Wavefront arg-max under the order (higher value, then lower index).
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          float ov = __shfl_xor(bv, o, kWave);
-          int oi = __shfl_xor(bi, o, kWave);
-          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
-        sel_v[k] = bv;
-        sel_i[k] = bi;
-        if ((bi & 63) == lane) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if ((bi >> 6) == c) v[c] = -INFINITY;
-        }
+    for (int j = 0; j < 4; ++j) {
+      if (tt[j] < T && lane < K) {
+        w.topk_idx[(size_t)tt[j] * K + lane] = ix[j];
+        w.topk_w[(size_t)tt[j] * K + lane] = wv[j];
+        atomicAdd(&hist[ix[j]], 1);
       }
     }
-    // Renormalised softmax over the selected logits (sel_v[0] is the maximum).
-    float den = 0.f, mine_w = 0.f;
-    int mine_i = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k < K) {
-        float p = __expf(sel_v[k] - sel_v[0]);
-        den += p;
-        if (lane == k) { mine_w = p; mine_i = sel_i[k]; }
-      }
-    }
-    if (lane < K) {
-      w.topk_idx[(size_t)t * K + lane] = mine_i;
-      w.topk_w[(size_t)t * K + lane] = mine_w / den;
-      atomicAdd(&hist[mine_i], 1);
-    }
-    // Shared-expert gate: sigmoid(x[t] . w_sg), four elements per lane per step.
-    float part = 0.f;
-    const bf16_t* xr = x + (size_t)t * H;
-    for (int h0 = 4 * lane; h0 < H; h0 += 256) {
-      uint2 xv = *reinterpret_cast<const uint2*>(xr + h0);
-      uint2 gv = *reinterpret_cast<const uint2*>(L.sh_expert_gate + h0);
-      part += bf16_to_f32(xv.x & 0xFFFFu) * bf16_to_f32(gv.x & 0xFFFFu);
-      part += bf16_to_f32(xv.x >> 16) * bf16_to_f32(gv.x >> 16);
-      part += bf16_to_f32(xv.y & 0xFFFFu) * bf16_to_f32(gv.y & 0xFFFFu);
-      part += bf16_to_f32(xv.y >> 16) * bf16_to_f32(gv.y >> 16);
-    }
-    part = wave_sum(part);
-    if (lane == 0) w.gate_s[t] = sigmoidf_(part);
   }
   __syncthreads();
   if (tid < E) w.blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
@@ -190,10 +187,21 @@ __global__ __launch_bounds__(256) void router_topk_kernel(LayerArgs L, const bf1
 
 }  // namespace
 
+int router_ksplit(int T, int H) {
+  const int ntiles = router_blocks(T);
+  int s = 1;
+  while (2 * s <= H / 64 && 2 * s <= 16 && ntiles * s < 256) s *= 2;
+  return s;
+}
+
 hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
                          float* logits_out, hipStream_t s) {
-  const int nblk = router_blocks(T);
-  hipLaunchKernelGGL(router_topk_kernel, dim3(nblk), dim3(256), 0, s, L, x, T, w, logits_out);
+  const int nblk = router_blocks(T), ks = router_ksplit(T, L.H);
+  hipLaunchKernelGGL(router_logits_kernel, dim3(nblk, ks), dim3(256), 0, s, L, x, T, ks, w.rlog);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(router_select_kernel, dim3(nblk), dim3(256), 0, s, L, T, ks, (const float*)w.rlog, w,
+                     logits_out);
   return hipGetLastError();
 }
 
