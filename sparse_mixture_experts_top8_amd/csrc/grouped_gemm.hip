@@ -12,12 +12,14 @@
 // sigmoid(Linear(x, 1))); Linnet model page, Blocks: SparseMoe
 // (gate_up_proj [E, 2I, H], down_proj [E, H, I]) and SwiGlu.
 //
-// One workgroup per tile of 128 rows x 128 weight rows; two workgroups share
-// a CU, so one's start-up overlaps the other's streaming.  Wave w owns weight
+// One workgroup per tile of 160 rows x 128 weight rows (160 rows hold a
+// typical expert of a 4096-token batch, about 128 +- 11 rows, in one tile, so
+// its weights stream once); two workgroups share a CU, so one's start-up
+// overlaps the other's streaming.  Wave w owns weight
 // rows 32w .. 32w + 31 of the tile as two 16-column MFMA blocks: for gate_up
 // the gate rows and the up rows of the same 16 inner rows (SiLU(g) * u is
 // formed in registers, both blocks having the same layout), for down 32 output
-// columns.  Each wave covers all 128 rows.
+// columns.  Each wave covers all 160 rows.
 //
 // k advances in steps of 64 through a four-deep ring, three steps in flight:
 // the weight fragments of a wave are needed by that wave alone and go straight
@@ -43,16 +45,21 @@
 // block, run side by side in one XCD and share them through its L2.
 #include "kernels.hpp"
 
+#include <utility>
+
 namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;      // 128 rows
+constexpr int BM = kGemmBM;      // 160 rows
 constexpr int BN = kGemmBNW;     // 128 weight rows
 constexpr int BK = 64;
 constexpr int NS = 4;            // ring depth (activation LDS stages = weight register slots)
-constexpr int kATile = BM * BK * 2;     // 16 KB
-constexpr int kVmPerStep = 4 + 4;       // per wave: 4 direct-to-LDS + 4 weight loads
+constexpr int kATile = BM * BK * 2;     // 20 KB
+constexpr int kMBlocks = BM / 16;       // 16-row MFMA blocks
+constexpr int kADma = BM * 8 / 256;     // direct-to-LDS instructions per wave per step (16-byte units / 256 threads)
+constexpr int kVmPerStep = kADma + 4;   // per wave: activation loads + 4 weight loads
+static_assert(kMBlocks == 10 && (BM * 8) % 256 == 0, "the step reads the tile rows in two groups of five blocks");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -60,18 +67,23 @@ constexpr uint32_t kOutside = 0x80000000u;
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+template <int OFF>
 __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
   u32x4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
   return v;
+}
+// Operands of five consecutive 16-row blocks I0 .. I0 + 4: one base address
+// per lane, the blocks 2048 bytes apart (16 rows of 128 bytes; the chunk
+// swizzle depends on row % 8 only, which is the same in every block).
+template <int I0, int... I>
+__device__ __forceinline__ void lds_read_group(u32x4 (&a)[5], uint32_t addr, std::integer_sequence<int, I...>) {
+  ((a[I] = lds_read16<2048 * (I0 + I)>(addr)), ...);
 }
 // Waits for the LDS reads and ties their result registers to the wait, so
 // that no use of them can be scheduled before it.
-__device__ __forceinline__ void wait_lds(u32x4 (&a)[8]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
-               :
-               : "memory");
+__device__ __forceinline__ void wait_lds(u32x4 (&a)[5]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]) : : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
@@ -119,12 +131,13 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
   const int l16 = lane & 15, q = lane >> 4;
   const uint32_t lds_base = (uint32_t)(size_t)(lds_ptr_t)lds;
 
-  // ---- activation sources: direct-to-LDS instruction j (0..3) of wave w
-  // writes 16-byte unit p = 64 (4 j + w) + lane, i.e. row r = 8 (4 j + w) +
-  // lane / 8, stored chunk lane % 8, holding the global chunk (lane % 8) ^ (r & 7).
-  const bf16_t* a_src[4];
+  // ---- activation sources: direct-to-LDS instruction j (0..kADma-1) of
+  // wave w writes 16-byte unit p = 64 (4 j + w) + lane, i.e. row
+  // r = 8 (4 j + w) + lane / 8, stored chunk lane % 8, holding the global
+  // chunk (lane % 8) ^ (r & 7).
+  const bf16_t* a_src[kADma];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kADma; ++j) {
     const int r = 8 * (4 * j + wv) + (lane >> 3);
     const int gch = ((lane & 7) ^ (r & 7)) * 8;
     const int row = m0 + min(r, rows_here - 1);         // rows past the group repeat its last row
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
     char* sbase = lds + st * kATile;
     const int kv = min(ks, nreal - 1);          // padding steps re-read the last real step
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kADma; ++j)
       __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + kv * BK), (lds_ptr_t)(sbase + 1024 * (4 * j + wv)),
                                        16, 0, 0);
     const bool real = ks < nreal;
@@ -175,9 +188,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
             b_rs[b], real ? b_off[b] + 2u * (uint32_t)(ks * BK + 8 * h) : kOutside, 0, 0);
   };
 
-  f32x4 acc[8][2];
+  f32x4 acc[kMBlocks][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kMBlocks; ++i)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[i][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int mblocks = (rows_here + 15) >> 4;    // 16-row blocks holding rows of the group
@@ -187,28 +200,33 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
   issue(wb[2], 2, 2);
   auto step = [&](u32x4 (&wcur)[2][2], u32x4 (&wnext)[2][2], int st, int ks) {
     // This step's loads must have landed; younger are the loads of the later
-    // steps already issued (at most two), 8 per step and wave.
+    // steps already issued (at most two), kVmPerStep per step and wave.
     const int younger = min(2, nsteps - 1 - ks);
     if (younger == 2) wait_vm<2 * kVmPerStep>();
     else if (younger == 1) wait_vm<kVmPerStep>();
     else wait_vm<0>();
     barrier();   // every wave's part of the stage is in LDS; the stage read last step is free
     if (ks + 3 < nsteps) issue(wnext, (st + 3) % NS, ks + 3);
-    const uint32_t sa = lds_base + st * kATile;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      u32x4 av[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ra = 16 * i + l16;
-        av[i] = lds_read16(sa + ra * 128 + (((2 * q + h) ^ (ra & 7)) << 4));
-      }
+      const uint32_t sa = lds_base + st * kATile + l16 * 128 + (((2 * q + h) ^ (l16 & 7)) << 4);
+      u32x4 av[5];
+      lds_read_group<0>(av, sa, std::make_integer_sequence<int, 5>{});
       wait_lds(av);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < mblocks) {
-          acc[i][0] = mfma16(av[i], wcur[0][h], acc[i][0]);
-          acc[i][1] = mfma16(av[i], wcur[1][h], acc[i][1]);
+      for (int i = 0; i < 5; ++i) {
+        acc[i][0] = mfma16(av[i], wcur[0][h], acc[i][0]);
+        acc[i][1] = mfma16(av[i], wcur[1][h], acc[i][1]);
+      }
+      // The second group of five 16-row blocks is skipped when the tile's rows
+      // end before it (uniform branch).
+      if (mblocks > 5) {
+        lds_read_group<5>(av, sa, std::make_integer_sequence<int, 5>{});
+        wait_lds(av);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          acc[5 + i][0] = mfma16(av[i], wcur[0][h], acc[5 + i][0]);
+          acc[5 + i][1] = mfma16(av[i], wcur[1][h], acc[5 + i][1]);
         }
       }
     }
@@ -229,10 +247,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
   // stores 16-byte row chunks; rows past the group fall outside the store
   // resource and are dropped.
   barrier();
-  bf16_t* ep = reinterpret_cast<bf16_t*>(lds + wv * (BM * 32 * 2));    // 128 rows x 32 columns (8 KB) per wave
+  bf16_t* ep = reinterpret_cast<bf16_t*>(lds + wv * (BM * 32 * 2));    // 160 rows x 32 columns (10 KB) per wave
   constexpr int kCols = GATE_UP ? 16 : 32;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kMBlocks; ++i)
 #pragma unroll
     for (int b = 0; b < (GATE_UP ? 1 : 2); ++b)
 #pragma unroll

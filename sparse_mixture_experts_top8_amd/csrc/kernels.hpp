@@ -9,7 +9,7 @@ namespace moe {
 // Router tile: tokens per router workgroup (also the dispatch block size).
 constexpr int kRouterTokens = 32;
 // Grouped-GEMM tile: rows (slots) per tile, weight rows per tile.
-constexpr int kGemmBM = 128;
+constexpr int kGemmBM = 160;
 constexpr int kGemmBNW = 128;   // weight rows per tile: gate_up 64 gate + 64 up; down 128 H cols
 // Upper bound of the tiles of one grouped GEMM (workspace and grid size):
 // every group adds at most one partial row tile.
