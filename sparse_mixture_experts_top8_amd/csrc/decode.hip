@@ -37,18 +37,18 @@
 // agent-scope release/acquire fences that keep plain stores coherent across
 // XCDs are L2 write-backs and invalidates, far too costly per hand-off.  Every
 // value one workgroup hands to another is written with agent-scope
-// (write-through) stores and read with device-scope buffer loads (sc1).  For
-// the h hand-off a workgroup arrives once all its waves' stores have completed
-// (s_waitcnt), by one atomic increment of its XCD's counter (eight counters on
-// separate 128-byte lines, so arrivals do not serialise on one address);
-// waiters poll the eight counters with one load.  The logits need no counter:
-// each is published as one 64-bit store of (value, tag).
+// (write-through) stores and read with device-scope buffer loads (sc1).
 //
-// Start protocol: the host passes a call-unique 64-bit epoch (low word never
-// 0, the tag).  Workgroup 0 zeroes the counters and then publishes the epoch;
-// every other workgroup sees the epoch before it touches a counter, so stale
-// values from an earlier call are never read.  Every wait is bounded in time
-// (see wait_until), so the grid always drains.
+// Every poll of the whole grid on a few shared lines queues at those lines'
+// memory channel, so what is polled is published once per XCD: the writer
+// stores eight copies, and the workgroups of XCD x poll copy x only.  The
+// logits are published as 64-bit (value, tag) words, the data being its own
+// flag.  For the h hand-off a workgroup whose stores have all completed
+// (s_waitcnt) writes the tag into its slot of each flag copy; waiters read
+// their copy's slots with one load per lane.  No atomics, no counters: the
+// tag is call-unique (the host's epoch, low word never 0), so words left by
+// earlier calls never match and nothing has to be cleared first.  Every wait
+// is bounded in time (see wait_until), so the grid always drains.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -67,12 +67,10 @@ constexpr int kBDepth = 2;               // gate/up blocks in flight per wave
 constexpr int kCDepth = 6;               // down groups in flight per wave
 constexpr unsigned long long kWaitTicks = 25000000ull;  // 0.25 s of the 100 MHz clock
 
-// Control block layout (uint32 words); every counter has its own 128-byte line.
-constexpr int kLine = 32;                // words per 128-byte line
-constexpr int kCtlEpoch = 0;             // 64-bit epoch in words 0-1
-constexpr int kCtlError = 1 * kLine;     // nonzero after a timed-out wait
-constexpr int kCtlBarB = 2 * kLine;      // + kLine * x: arrivals at the h hand-off from XCD x
-static_assert(kDecodeCtlWords >= 10 * kLine, "control block too small");
+// Control block layout (uint32 words).
+constexpr int kCtlError = 0;             // 0, or the call's tag once one of its waits timed out
+constexpr int kCtlFlags = 32;            // + x * kDecodeFlagStride: copy x of the arrival flags
+static_assert(kDecodeCtlWords >= kCtlFlags + kDecodeReplicas * kDecodeFlagStride, "control block too small");
 
 // Weight fragment (plain load: on MI355X the non-temporal hint measured
 // slower for these streams).
@@ -126,12 +124,12 @@ __device__ __forceinline__ void stores_complete() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Bounded wait: gives up after kWaitTicks (or at once once any wave gave up),
-// records `code` in the error word and returns; indices read from shared state
-// are clamped by their users, so a timed-out wait yields wrong numbers, never
-// an out-of-bounds access.
+// Bounded wait: gives up after kWaitTicks (or soon after another wave of the
+// call gave up), records the call's tag in the error word and returns; indices
+// read from shared state are clamped by their users, so a timed-out wait
+// yields wrong numbers, never an out-of-bounds access.
 template <typename Ready>
-__device__ __forceinline__ void wait_until(Ready ready, uint32_t* err, uint32_t code) {
+__device__ __forceinline__ void wait_until(Ready ready, uint32_t* err, uint32_t tag) {
   if (!ready()) {
     const unsigned long long t0 = wall_clock64();
     uint32_t n = 0;
@@ -139,8 +137,8 @@ __device__ __forceinline__ void wait_until(Ready ready, uint32_t* err, uint32_t 
       // A short back-off: every workgroup polls the same few lines, and
       // tighter polling only queues more requests in front of the writes.
       __builtin_amdgcn_s_sleep(4);
-      if ((++n & 63u) == 0u && (ld_cnt(err) != 0u || wall_clock64() - t0 > kWaitTicks)) {
-        __hip_atomic_fetch_or(err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((++n & 63u) == 0u && (ld_cnt(err) == tag || wall_clock64() - t0 > kWaitTicks)) {
+        st_dev(err, tag);
         break;
       }
     }
@@ -172,7 +170,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int kbeg = wave * (H / 4);
   uint32_t* ctl = a.ctl;
   uint32_t* err = ctl + kCtlError;
-  unsigned long long* epoch_p = reinterpret_cast<unsigned long long*>(ctl + kCtlEpoch);
+  const uint32_t tag = (uint32_t)a.epoch;
+  // This workgroup's XCD picks the copy of published data it polls.
+  const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID[3:0]
+  const int lstride = decode_logit_stride(T);
   const f32x4 zf4 = {0.f, 0.f, 0.f, 0.f};
 
   __shared__ __attribute__((aligned(16))) bf16_t s_x[kMaxT * kXStride];   // x, one padded row per token
@@ -187,24 +188,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __shared__ int s_vg[256 + kMaxT * 8 / 8];    // routed chunks: (u << 16) | (first pair << 8) | pairs (<= 8)
   __shared__ int s_U, s_NV;
 
-  // ---------------- start: counters zeroed, then the epoch published ----------------
-  if (wg == 0) {
-    for (int i = tid; i < 9; i += kThreads)
-      __hip_atomic_store(ctl + kCtlError + kLine * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    stores_complete();
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(epoch_p, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  const uint32_t tag = (uint32_t)a.epoch;
-  bool epoch_seen = false;   // meaningful in wave 0
-  auto see_epoch = [&]() {
-    if (!epoch_seen) {
-      wait_until([&] { return __hip_atomic_load(epoch_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch; },
-                 err, 2u);
-      epoch_seen = true;
-    }
-  };
-
+  // The error word is cleared at the start of every call (a timed-out wait
+  // sets it only after kWaitTicks, long after this store).
+  if (wg == 0 && tid == 0) st_dev(err, 0u);
   for (int i = tid; i < 256; i += kThreads) s_mask[i] = 0u;
   for (int i = tid; i < kWaves * 16 * kMaxT; i += kThreads) (&s_acc[0][0][0])[i] = 0.f;
 
@@ -280,7 +266,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           const int e = r_lo + mm;
           const float v = tile(mm);
           if (e < E) {
-            st_dev(a.logits_t + (size_t)n * E + e, ((uint64_t)__float_as_uint(v) << 32) | tag);
+            // Slot 64 (e % 4) + e / 4 of the token's row: the reader lane that
+            // owns experts 4 l .. 4 l + 3 finds them 512 bytes apart, so each
+            // of its four loads covers four whole lines.
+            const uint64_t tv = ((uint64_t)__float_as_uint(v) << 32) | tag;
+            uint64_t* dst = a.logits_t + (size_t)n * 256 + 64 * (e & 3) + (e >> 2);
+#pragma unroll
+            for (int x = 0; x < kDecodeReplicas; ++x) st_dev(dst + (size_t)x * lstride, tv);
             if (a.logits_out) a.logits_out[(size_t)n * E + e] = v;
           } else {
             st_dev(a.gate_s + n, sigmoidf_(v));
@@ -295,10 +287,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
   // ---------------- phase K: top-K selections into LDS ----------------
   // Wave w handles tokens w, w + 4, ... (NT of them, lane: experts 4 lane ..
-  // 4 lane + 3): it polls their tagged logits until every one carries this
-  // call's tag, then selects the top-K of all of them together.
+  // 4 lane + 3): it polls their tagged logits (its XCD's copy) until every one
+  // carries this call's tag, then selects the top-K of all of them together.
   {
-    const rsrc_t r_lt = make_rsrc(a.logits_t, (size_t)T * E * 8);
+    const rsrc_t r_lt = make_rsrc(a.logits_t + (size_t)xcc * lstride, (size_t)T * 256 * 8);
     auto run = [&](auto nt_tag) {
       constexpr int NT = decltype(nt_tag)::value;
       uint64_t sl[NT][4];
@@ -312,14 +304,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             const int e = 4 * lane + c;
             const bool in = e < E && t < T;
             // One 64-bit load: value and tag come from the same store.
-            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(r_lt, in ? 8u * (uint32_t)(t * E + e) : kOutside, 0, 16);
+            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(
+                r_lt, in ? 8u * (uint32_t)(t * 256 + 64 * c + lane) : kOutside, 0, 16);
             sl[j][c] = ((uint64_t)w2[1] << 32) | w2[0];
             ok = ok && (!in || (uint32_t)sl[j][c] == tag);
           }
         }
         return __ballot(!ok) == 0ull;
       };
-      wait_until(ready, err, 4u);
+      wait_until(ready, err, tag);
       float lv[NT][4];
 #pragma unroll
       for (int j = 0; j < NT; ++j)
@@ -533,19 +526,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 
   // ---------------- h hand-off ----------------
-  // Every wave's stores (h, and h_sh from phase A) are complete, then one
-  // arrival for this workgroup on its XCD's counter; wave 0 waits until every
-  // workgroup has arrived (lane x polls XCD x's counter) and the barrier
-  // releases the other waves.
+  // Every wave's stores (h, and h_sh from phase A) are complete, then wave 0
+  // writes the tag into this workgroup's slot of every flag copy and waits
+  // until all G slots of its XCD's copy carry it (lane l reads slots
+  // 4 l .. 4 l + 3); the barrier releases the other waves.
   stores_complete();
   __syncthreads();
   if (wave == 0) {
-    see_epoch();
-    if (lane == 0)
-      __hip_atomic_fetch_add(ctl + kCtlBarB + kLine * (wg & 7), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int x = lane & 7;
-    const uint32_t need = x < G ? (uint32_t)((G - x + 7) / 8) : 0u;
-    wait_until([&] { return __ballot(ld_cnt(ctl + kCtlBarB + kLine * x) < need) == 0ull; }, err, 1u);
+    if (lane < kDecodeReplicas) st_dev(ctl + kCtlFlags + lane * kDecodeFlagStride + wg, tag);
+    const rsrc_t r_fl = make_rsrc(ctl + kCtlFlags + xcc * kDecodeFlagStride, (size_t)G * 4);
+    wait_until(
+        [&] {
+          const auto f = __builtin_amdgcn_raw_buffer_load_b128(r_fl, 16u * (uint32_t)lane, 0, 16);
+          bool ok = true;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ok = ok && (4 * lane + c >= G || f[c] == tag);
+          return __ballot(!ok) == 0ull;
+        },
+        err, tag);
   }
   __syncthreads();
 
@@ -633,7 +631,7 @@ int decode_max_grid(int num_cus) {
 }
 
 bool decode_fits(int H, int E, int Is, int grid) {
-  if (grid < 1) return false;
+  if (grid < 1 || grid > kDecodeMaxGrid) return false;
   const int rows_a = (E + 1 + grid - 1) / grid + 1 + 2 * ((Is + grid - 1) / grid);
   const int rows_c = (H + grid - 1) / grid;
   return rows_a <= 16 && rows_c <= 8;

@@ -34,8 +34,9 @@ struct DecodeArgs {
   int T;
   int route_only;       // 1: stop after routing and write offsets/perm
   bf16_t* out;          // [T, H]
-  uint32_t* ctl;        // control block: epoch, counters, error word
-  uint64_t* logits_t;   // [T, E] tagged logits: fp32 bits in the high word, the call tag in the low word
+  uint32_t* ctl;        // control block: error word, arrival flags (kDecodeReplicas copies)
+  uint64_t* logits_t;   // kDecodeReplicas copies of [T, 256] tagged logits (fp32 bits in the high
+                        // word, the call tag in the low word), copy stride decode_logit_stride(T)
   float* logits_out;    // optional [T, E] fp32 logits (route)
   int32_t* topk_idx;    // [T, K]
   float* topk_w;        // [T, K]
@@ -46,7 +47,14 @@ struct DecodeArgs {
   int32_t* perm_out;    // route-only: [T*K]
   unsigned long long epoch;   // call-unique; its low 32 bits (never 0) tag this call's logits
 };
-constexpr int kDecodeCtlWords = 18 * 32;  // epoch, error word, 16 counters: one 128-byte line each
+// Cross-workgroup data of the decode path is published in one copy per XCD
+// (readers poll the copy of their own XCD).
+constexpr int kDecodeReplicas = 8;
+constexpr int kDecodeMaxGrid = 256;
+constexpr int kDecodeFlagStride = kDecodeMaxGrid + 32;   // words between flag copies
+constexpr int kDecodeCtlWords = 32 + kDecodeReplicas * kDecodeFlagStride;
+// Elements (uint64) between logit copies: T rows of 256, plus a 512-byte skew.
+__host__ __device__ inline int decode_logit_stride(int T) { return T * 256 + 64; }
 
 hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s);
 int decode_max_grid(int num_cus);

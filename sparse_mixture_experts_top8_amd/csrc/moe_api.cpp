@@ -121,7 +121,7 @@ DecodeCarve carve_decode(const moe_layer_t* L, int64_t T, char* base) {
   };
   DecodeCarve c{};
   c.ctl = (uint32_t*)take(moe::kDecodeCtlWords * 4);
-  c.logits_t = (uint64_t*)take(t * E * 8);
+  c.logits_t = (uint64_t*)take((size_t)moe::kDecodeReplicas * moe::decode_logit_stride((int)t) * 8);
   c.topk_idx = (int32_t*)take(tk * 4);
   c.topk_w = (float*)take(tk * 4);
   c.gate_s = (float*)take(t * 4);

@@ -96,9 +96,9 @@ def check_output(xb, bits, dims, gi, out_rows, rows, tag):
 
 
 def decode_error_word(ws):
-    """The fused decode path keeps a status word in the workspace (bytes 128-131):
-    nonzero if any wait inside the kernel timed out."""
-    return int(ws[128:132].cpu().view(torch.int32)[0])
+    """The fused decode path keeps a status word in the workspace (bytes 0-3),
+    cleared at the start of each call: nonzero if any wait inside it timed out."""
+    return int(ws[0:4].cpu().view(torch.int32)[0])
 
 
 def run_layer(layer, xb, want_logits=False):
