@@ -33,107 +33,99 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float siluf_(float z) { return z / (1.0f + __expf(-z)); }
 
-// ---- wavefront reductions on DPP lane moves (no LDS traffic) ----
-// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror and row_mirror
-// combine lanes inside each 16-lane row (after the four steps every lane of a
-// row holds the row's result); the four row results are then read into
-// scalar registers and combined, so every lane returns the same value.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
-}
-__device__ __forceinline__ float row_lane_f(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  v += dpp_f<0x140>(v);
-  return (row_lane_f(v, 0) + row_lane_f(v, 16)) + (row_lane_f(v, 32) + row_lane_f(v, 48));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
-  return fmaxf(fmaxf(row_lane_f(v, 0), row_lane_f(v, 16)), fmaxf(row_lane_f(v, 32), row_lane_f(v, 48)));
-}
-
-__device__ __forceinline__ int wave_min_i(int v) {
-  v = min(v, dpp_i<0xB1>(v));
-  v = min(v, dpp_i<0x4E>(v));
-  v = min(v, dpp_i<0x141>(v));
-  v = min(v, dpp_i<0x140>(v));
-  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-
-// Arg-max over the wave under the order (higher value, then lower index):
-// lane-local candidates (bv, bi) in, the winner's value and index out (uniform).
-__device__ __forceinline__ void wave_argmax(float bv, int bi, float* v_out, int* i_out) {
-  const float m = wave_max(bv);
-  *i_out = wave_min_i(bv == m ? bi : 0x7FFFFFFF);
-  *v_out = m;
-}
-
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
-// Top-K of NT tokens by one wave (independent chains, interleaved), from each
-// lane's four logits of experts 4 lane + c: descending logit, ties to the
-// lower expert index (the lowest lane among equal lane bests, the lowest c
-// inside a lane); lane k < K receives the k-th index and its weight, the
-// softmax over the selected logits (equal to the full softmax renormalised).
-// A validity mask (experts < E, not yet taken) keeps every pick distinct even
-// among equal or -inf values; NaN counts as -inf.
+// Orderable 32-bit key of a logit: a larger logit has a larger key, NaN counts
+// as -inf and -0 as +0, so two keys are equal exactly when the logits compare
+// equal.  Every key is >= key(-inf) = 0x007FFFFF, above the 0 used for
+// experts that do not exist (and for candidates already taken).
+__device__ __forceinline__ uint32_t logit_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (f != f) b = 0xFF800000u;
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+// Maximum of an unsigned value over the wave, in every lane: four DPP steps
+// inside each 16-lane row (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror), then the four row results through scalar
+// registers.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x141>(v));
+  v = max(v, dpp_u<0x140>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Top-K (K <= 8) of NT tokens by one wave (independent chains, interleaved),
+// from each lane's four logits of experts 4 lane + c: order by descending
+// logit, ties to the lower expert index; lane k < K receives the k-th index
+// and its weight, the softmax over the selected logits (equal to the full
+// softmax renormalised over them), its denominator summed in rank order.
+//
+// Each lane first sorts its four keys (descending, lower c first among equal
+// keys), so its best remaining candidate is always its head.  A pick is the
+// wave maximum of the heads; among equal heads the lowest lane wins, which is
+// the lowest expert index (a lane holding that key anywhere holds it at its
+// head).  The winner's head then moves on to its next key.
 template <int NT>
 __device__ __forceinline__ void topk_select(const float (&lv)[NT][4], int E, int K, int lane, int (&idx_out)[NT],
                                             float (&w_out)[NT]) {
-  float v[NT][4];
-  uint32_t valid[NT];
-  float vmax[NT], den[NT], mine_v[NT];
-  int mine_i[NT];
+  uint32_t hk[NT][4];   // this lane's keys, sorted; 0 once used up (below every key)
+  uint32_t hc[NT];      // their c, two bits each, head in the low bits
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    valid[j] = 0u;
+    uint32_t k[4];
+    int c[4] = {0, 1, 2, 3};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v[j][c] = lv[j][c] == lv[j][c] ? lv[j][c] : -INFINITY;
-      if (4 * lane + c < E) valid[j] |= 1u << c;
-    }
-    vmax[j] = 0.f;
-    den[j] = 0.f;
-    mine_v[j] = 0.f;
-    mine_i[j] = 0;
+    for (int i = 0; i < 4; ++i) k[i] = 4 * lane + i < E ? logit_key(lv[j][i]) : 0u;
+    // Five compare-exchanges; (key, c) compared as key descending, c ascending.
+    auto cx = [&](int a, int b) {
+      const bool sw = k[b] > k[a] || (k[b] == k[a] && c[b] < c[a]);
+      const uint32_t ka = k[a], kb = k[b];
+      const int ca = c[a], cb = c[b];
+      k[a] = sw ? kb : ka; k[b] = sw ? ka : kb;
+      c[a] = sw ? cb : ca; c[b] = sw ? ca : cb;
+    };
+    cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hk[j][i] = k[i];
+    hc[j] = (uint32_t)(c[0] | (c[1] << 2) | (c[2] << 4) | (c[3] << 6));
   }
+  uint32_t my_key[NT], my_idx[NT], first_key[NT];
+  float den[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) { my_key[j] = 0u; my_idx[j] = 0u; first_key[j] = 0u; den[j] = 0.f; }
   for (int k = 0; k < K; ++k) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      float bv = -INFINITY;
-      int bc = -1;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (((valid[j] >> c) & 1u) && (bc < 0 || v[j][c] > bv)) { bv = v[j][c]; bc = c; }
-      const float mx = wave_max(bv);
-      const unsigned long long win = __ballot(bc >= 0 && bv == mx);
-      const int wl = (int)__builtin_ctzll(win);
-      const int wc = __builtin_amdgcn_readlane(bc, wl);
-      if (lane == wl) valid[j] &= ~(1u << wc);
-      if (k == 0) vmax[j] = mx;
-      den[j] += __expf(mx - vmax[j]);
-      if (lane == k) { mine_v[j] = mx; mine_i[j] = 4 * wl + wc; }
+      const uint32_t m = wave_max_u32(hk[j][0]);
+      const int wl = (int)__builtin_ctzll(__ballot(hk[j][0] == m));
+      const uint32_t wc = (uint32_t)__builtin_amdgcn_readlane((int)hc[j], wl) & 3u;
+      const bool won = lane == wl;
+      hk[j][0] = won ? hk[j][1] : hk[j][0];
+      hk[j][1] = won ? hk[j][2] : hk[j][1];
+      hk[j][2] = won ? hk[j][3] : hk[j][2];
+      hk[j][3] = won ? 0u : hk[j][3];
+      hc[j] = won ? hc[j] >> 2 : hc[j];
+      if (k == 0) first_key[j] = m;
+      den[j] += __expf(key_logit(m) - key_logit(first_key[j]));
+      if (lane == k) { my_key[j] = m; my_idx[j] = 4u * (uint32_t)wl + wc; }
     }
   }
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    idx_out[j] = clamp_expert(mine_i[j], E);
-    w_out[j] = __expf(mine_v[j] - vmax[j]) / den[j];
+    idx_out[j] = clamp_expert((int)my_idx[j], E);
+    w_out[j] = __expf(key_logit(my_key[j]) - key_logit(first_key[j])) / den[j];
   }
 }
 

@@ -158,6 +158,34 @@ def test_toy_zero_input_all_ties(toy):
     assert np.all(_np(out.float()) == 0.0)
 
 
+def test_toy_duplicate_router_rows_tie_to_lower_index():
+    # Router rows 2j and 2j+1 identical: their logits are equal bit for bit on
+    # both paths, so whenever expert 2j+1 is chosen, 2j must be chosen right
+    # before it with the same weight (ties go to the lower expert index).
+    moe = _moe()
+    for E, K in [(16, 4), (256, 8)]:
+        d = mi.Dims(H=256, E=E, K=K, I=64, Is=64)
+        bits = mi.make_layer(d, 900 + E)
+        g = bits["gate.weight"].copy()
+        g[1::2] = g[0::2]
+        bits["gate.weight"] = g
+        layer = moe.MoeLayer.from_bf16_bits(bits, d.H, d.E, d.K, d.I, d.Is, "cuda")
+        for T in (1, 5, 16, 100):
+            _say(f"case toy duplicate router rows E={E} K={K} T={T}")
+            xb = mi.make_x(d, T, 950 + T)
+            r, _ = run_layer(layer, xb)
+            gi, gw = _np(r["topk_idx"]), _np(r["topk_w"])
+            for t in range(T):
+                for k in range(K):
+                    e = int(gi[t, k])
+                    if e % 2 == 1:
+                        assert k > 0 and gi[t, k - 1] == e - 1, (E, T, t, gi[t])
+                        assert gw[t, k - 1] == gw[t, k], (E, T, t, gw[t])
+                    elif k + 1 < K and gi[t, k + 1] == e + 1:
+                        assert gw[t, k + 1] == gw[t, k]
+            check_routing(xb, bits, d, r, f"dup rows E={E} T={T}")
+
+
 def test_toy_other_k_and_e():
     moe = _moe()
     for (E, K) in [(8, 8), (16, 1), (32, 8), (256, 8)]:
