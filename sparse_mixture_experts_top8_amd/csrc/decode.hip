@@ -26,12 +26,13 @@
 //      every touched expert, in a fixed order, then writes out.
 //
 // Weight streams are software pipelined: a wave keeps the loads of the next
-// blocks (phase B) or groups (phase C) in flight while it computes the current
-// one, and the down-projection weights of the first groups are requested before
-// hand-off B, since they do not depend on h.  Every tile is a 16 x 16 tile of
-// v_mfma_f32_16x16x32_bf16 whose columns are tokens (or one expert's pairs),
-// with the contraction split over the four waves; partial tiles meet in LDS in
-// a fixed order, so results are bitwise reproducible.
+// blocks (phase B) or stages (phase C) in flight while it computes the current
+// one, and the down-projection weights of the first stages are requested during
+// phase B, since they do not depend on h.  Every tile is a 16 x 16 tile of
+// v_mfma_f32_16x16x32_bf16 whose columns are tokens (phases A and C) or one
+// expert's pairs (phase B), with the contraction split over the four waves;
+// partial tiles meet in LDS in a fixed order, so results are bitwise
+// reproducible.
 //
 // Cross-workgroup data on MI355X: each XCD has its own write-back L2, and the
 // agent-scope release/acquire fences that keep plain stores coherent across
@@ -64,7 +65,8 @@ constexpr int kMaxHSteps = 16;           // 32-wide k-steps in one wave's quarte
 constexpr int kMaxISteps = 4;            // 32-wide k-steps in one wave's quarter of an inner dim (<= 512)
 constexpr int kXStride = 2048 + 8;       // LDS row stride of x, bf16 elements (rows stay 16-byte aligned)
 constexpr int kBDepth = 2;               // gate/up blocks in flight per wave
-constexpr int kCDepth = 6;               // down groups in flight per wave
+constexpr int kCDepth = 6;               // down-projection stages in flight per wave
+constexpr int kMaxCStages = 1 + 8 * 8;   // shared expert + one stage per expert touched by 8 tokens
 constexpr unsigned long long kWaitTicks = 25000000ull;  // 0.25 s of the 100 MHz clock
 
 // Control block layout (uint32 words).
@@ -178,21 +180,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
   __shared__ __attribute__((aligned(16))) bf16_t s_x[kMaxT * kXStride];   // x, one padded row per token
   __shared__ f32x4 s_red[2][kWaves][kWave];     // partial tiles of the four waves (two blocks in flight)
-  __shared__ float s_acc[kWaves][16][kMaxT];    // phase C: per-wave output accumulators
   __shared__ uint32_t s_mask[256];              // tokens that selected expert e (bit t)
   __shared__ int s_off[257];                    // pair-list offsets per expert
   __shared__ int s_touched[256];                // touched experts, ascending
   __shared__ int s_list[kMaxT * 8];             // pair ids grouped by expert, pair-id order inside
   __shared__ int s_tidx[kMaxT * 8];
   __shared__ float s_tw[kMaxT * 8];
-  __shared__ int s_vg[256 + kMaxT * 8 / 8];    // routed chunks: (u << 16) | (first pair << 8) | pairs (<= 8)
-  __shared__ int s_U, s_NV;
+  __shared__ int s_cq[kMaxCStages * 16];       // phase C: h row of each stage's tile column (-1: none)
+  __shared__ int s_tl[2][64];                   // experts touched by tokens 0-7 / 8-15, ascending (T > 8)
+  __shared__ int s_U, s_U01;
 
   // The error word is cleared at the start of every call (a timed-out wait
   // sets it only after kWaitTicks, long after this store).
   if (wg == 0 && tid == 0) st_dev(err, 0u);
   for (int i = tid; i < 256; i += kThreads) s_mask[i] = 0u;
-  for (int i = tid; i < kWaves * 16 * kMaxT; i += kThreads) (&s_acc[0][0][0])[i] = 0.f;
 
   // ---------------- phase A: router rows and shared-expert rows ----------------
   // Workgroup wg owns router rows [r_lo, r_hi) of E + 1 (row E: the shared
@@ -336,46 +337,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   // ---------------- phase L: per-expert pair lists in LDS ----------------
-  // Token masks per expert, then offsets and the touched list from one scan
-  // (low half: pair counts, high half: touched flags), then each pair's slot:
-  // its expert's offset plus the number of earlier tokens with that expert.
+  // Token masks per expert, then offsets and the touched list (ascending
+  // expert) from one scan (low half: pair counts, high half: touched flags),
+  // then each pair's slot: its expert's offset plus the number of earlier
+  // tokens with that expert.
   for (int q = tid; q < TK; q += kThreads) atomicOr(&s_mask[s_tidx[q]], 1u << (q / K));
   __syncthreads();
   if (wave == 0) {
-    int v4[4], run = 0;
+    // Second scan: touched flags per token group (tokens 0-7 low half, 8-15
+    // high half) for phase C with T > 8.
+    int v4[4], g4[4], run = 0, grun = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
-      const int c = e < E ? __popc(s_mask[e]) : 0;
+      const uint32_t mk = e < E ? s_mask[e] : 0u;
+      const int c = __popc(mk);
       v4[j] = c | ((c > 0 ? 1 : 0) << 16);
+      g4[j] = ((mk & 0xFFu) ? 1 : 0) | ((mk & 0xFF00u) ? 1 << 16 : 0);
       run += v4[j];
+      grun += g4[j];
     }
     const int incl = wave_incl_scan(run, lane);
-    // Chunks of at most 8 pairs per touched expert (phase C tiles).
-    int n4[4], nrun = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      n4[j] = ((v4[j] & 0xFFFF) + 7) >> 3;
-      nrun += n4[j];
-    }
-    const int nincl = wave_incl_scan(nrun, lane);
-    int ex = incl - run, nex = nincl - nrun;
+    const int gincl = wave_incl_scan(grun, lane);
+    int ex = incl - run, gx = gincl - grun;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
       if (e < E) {
         s_off[e] = ex & 0xFFFF;
-        const int c = v4[j] & 0xFFFF;
-        if (c) {
-          const int u = ex >> 16;
-          s_touched[u] = e;
-          for (int k = 0; k < n4[j]; ++k) s_vg[nex + k] = (u << 16) | ((8 * k) << 8) | min(8, c - 8 * k);
-        }
+        if (v4[j] & 0xFFFF) s_touched[ex >> 16] = e;
+        if (g4[j] & 0xFFFF) s_tl[0][gx & 0xFFFF] = e;
+        if (g4[j] >> 16) s_tl[1][gx >> 16] = e;
       }
       ex += v4[j];
-      nex += n4[j];
+      gx += g4[j];
     }
-    if (lane == 63) { s_off[E] = incl & 0xFFFF; s_U = incl >> 16; s_NV = nincl; }
+    if (lane == 63) { s_off[E] = incl & 0xFFFF; s_U = incl >> 16; s_U01 = gincl; }
   }
   __syncthreads();
   for (int q = tid; q < TK; q += kThreads) {
@@ -397,63 +394,55 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   const int U = s_U;
 
-  const int NV = s_NV;
 
   // Phase C geometry (its first weights are requested during phase B).
-  // Workgroup wg owns output rows [row0, row0 + nrows), nrows <= 8.  A tile
-  // holds two independent 8-row halves: tile rows 8h + r are output row r of
-  // half h, tile columns 8h + p are pair p of half h, and only the two
-  // diagonal 8 x 8 blocks of the product are used.  Stage 0 is the shared
-  // expert (columns: tokens 0-7 and 8-15; h_sh already carries the gate);
-  // stage s >= 1 holds routed chunks 2 (s - 1) and 2 (s - 1) + 1 (columns: the
-  // chunk's pairs; h already weighted).  Wave w takes k-steps [4w, 4w + 4) of
-  // the inner dimension.
+  // Workgroup wg owns output rows [row0, row0 + nrows), nrows <= 8.  Its down
+  // projection is one contraction over (segment, inner index) -- segment 0 the
+  // shared expert, segment 1 + u the u-th touched expert -- with tokens as
+  // tile columns, so every stage adds into the same accumulator tile.  A tile
+  // has two 8-row halves: row 8 h + r is output row r, column 8 h + j token
+  // tb(h) + j, and only the two diagonal 8 x 8 blocks of the product are used.
+  // With T <= 8 the halves take different experts (stage s >= 1: touched
+  // experts 2 (s - 1) + h), tb = 0, and the diagonal blocks are added at the
+  // end; with T > 8, tb(h) = 8 h and half h takes the (s - 1)-th expert
+  // touched by its own eight tokens.  Stage 0 is the shared expert (with
+  // T <= 8 in half 0 only; h_sh carries its gate, h the routing weight).
+  // Wave w takes k-steps [4 w, 4 w + 4) of the inner dimension.
+  const bool split_tok = T > 8;
+  const int U0 = s_U01 & 0xFFFF, U1 = s_U01 >> 16;
+  const int NS = 1 + (split_tok ? max(U0, U1) : (U + 1) / 2);
+  // Expert of half h at stage s >= 1, or -1.
+  auto stage_expert = [&](int s, int h) -> int {
+    if (split_tok) {
+      const int j = s - 1;
+      return j < (h ? U1 : U0) ? s_tl[h][j] : -1;
+    }
+    const int j = 2 * (s - 1) + h;
+    return j < U ? s_touched[j] : -1;
+  };
   const int rpw = (H + G - 1) / G;
   const int row0 = wg * rpw, nrows = max(0, min(rpw, H - row0));
-  const int NS = 1 + (NV + 1) / 2;
-  const int hm = m >> 3, pm = m & 7;     // this lane's A-row / B-column half and index in it
-  const int crow = min(row0 + min(pm, max(nrows, 1) - 1), H - 1);
+  const int hm = m >> 3, rm = m & 7;     // this lane's A-row (and B-column) half and index in it
+  const bool row_ok = rm < nrows;
+  const int crow = min(row0 + rm, H - 1);
   u32x4 ca[kCDepth][kMaxISteps], cb[kCDepth][kMaxISteps];
   const rsrc_t r_dn = make_rsrc(L.down_w, (size_t)E * H * I * 2);
   const rsrc_t r_sdn = make_rsrc(L.sh_down_w, (size_t)H * Is * 2);
-  // Column p of half h of stage s: its token and its h row (or -1).
-  auto column = [&](int s, int h, int p, int* tok) -> int {
-    if (s == 0) {
-      const int t = 8 * h + p;
-      *tok = t;
-      return t < T ? t : -1;
-    }
-    const int j = 2 * (s - 1) + h;
-    if (s >= NS || j >= NV) return -1;
-    const int v = s_vg[j];
-    if (p >= (v & 0xFF)) return -1;
-    const int q = s_list[s_off[s_touched[v >> 16]] + ((v >> 8) & 0xFF) + p];
-    *tok = q / K;
-    return q;
-  };
-  // This lane's column of the first stages (their h loads go out right after
-  // the hand-off).
-  int crow_h[kCDepth], ctok[kCDepth];
-#pragma unroll
-  for (int s = 0; s < kCDepth; ++s) {
-    int tok = 0;
-    crow_h[s] = column(s, hm, pm, &tok);
-    ctok[s] = crow_h[s] >= 0 ? tok : -1;
-  }
-  // Stages past the last one, empty halves and k-steps past the inner size
-  // load zeros from outside the resources.
+  // Down-projection weights of stage s for this lane's row (zeros from
+  // outside the resource for stages past the last, empty halves, rows past
+  // nrows and k-steps past the inner size).
   auto issue_a = [&](u32x4 (&st)[kMaxISteps], int s) {
-    const int nk = (s == 0 ? Is : I) / 32;
     uint32_t off = kOutside;
-    if (nrows > 0) {
+    if (row_ok && s < NS) {
       if (s == 0) {
-        off = 2u * (uint32_t)(crow * Is + kq);
+        if (split_tok || hm == 0) off = 2u * (uint32_t)(crow * Is + kq);
       } else {
-        const int j = 2 * (s - 1) + hm;
-        if (s < NS && j < NV) off = 2u * (uint32_t)((s_touched[s_vg[j] >> 16] * H + crow) * I + kq);
+        const int e = stage_expert(s, hm);
+        if (e >= 0) off = 2u * (uint32_t)((e * H + crow) * I + kq);
       }
     }
     const rsrc_t rs = s == 0 ? r_sdn : r_dn;
+    const int nk = (s == 0 ? Is : I) / 32;
 #pragma unroll
     for (int s4 = 0; s4 < kMaxISteps; ++s4) {
       const int ks = kMaxISteps * wave + s4;
@@ -517,6 +506,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // behind the first gate/up stages, so that they stream during phase B.
 #pragma unroll
     for (int s = 0; s < kCDepth; ++s) issue_a(ca[s], s);
+    // Phase C's B operands: for every stage and tile column the row of h
+    // (routed: the pair of that expert and token) or of h_sh (stage 0), or -1.
+    // Read after the hand-off barrier.
+    for (int i = tid; i < NS * 16; i += kThreads) {
+      const int sg = i >> 4, n = i & 15, hb = n >> 3;
+      const int t = (split_tok ? 8 * hb : 0) + (n & 7);
+      int q = -1;
+      if (t < T) {
+        if (sg == 0) {
+          if (split_tok || hb == 0) q = t;
+        } else {
+          const int e = stage_expert(sg, hb);
+          if (e >= 0) {
+            const uint32_t mk = s_mask[e];
+            if ((mk >> t) & 1u) q = s_list[s_off[e] + __popc(mk & ((1u << t) - 1u))];
+          }
+        }
+      }
+      s_cq[i] = q;
+    }
     for (int i = 0; i < nmine; i += 2) {
       compute(wa[0], i);
       issue(wa[0], i + 2);
@@ -532,6 +541,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // 4 l .. 4 l + 3); the barrier releases the other waves.
   stores_complete();
   __syncthreads();
+  // Rows of h for the first stages of phase C, read while the hand-off waits
+  // (the table was completed before the barrier above).
+  auto cq = [&](int s) {
+    const int q = s_cq[min(s, kMaxCStages - 1) * 16 + m];
+    return s < NS ? q : -1;
+  };
+  int q0[kCDepth];
+#pragma unroll
+  for (int s = 0; s < kCDepth; ++s) q0[s] = cq(s);
   if (wave == 0) {
     if (lane < kDecodeReplicas) st_dev(ctl + kCtlFlags + lane * kDecodeFlagStride + wg, tag);
     const rsrc_t r_fl = make_rsrc(ctl + kCtlFlags + xcc * kDecodeFlagStride, (size_t)G * 4);
@@ -548,15 +566,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   // ---------------- phase C: down projection and combine ----------------
-  // Each wave adds its partial tiles into its own LDS accumulator; the four
-  // are summed at the end.
   {
     const rsrc_t r_h = make_rsrc(a.h, (size_t)TK * I * 2);
     const rsrc_t r_hsh = make_rsrc(a.h_sh, (size_t)T * Is * 2);
-    // h rows (row r of h, or of h_sh in stage 0; r < 0: none) for stage s.
-    auto issue_b = [&](u32x4 (&st)[kMaxISteps], int s, int r) {
+    // h fragments of stage s for this lane's column (h row q, or none).
+    auto issue_b = [&](u32x4 (&st)[kMaxISteps], int s, int q) {
       const int inner = s == 0 ? Is : I, nk = inner / 32;
-      const uint32_t row = r >= 0 ? 2u * (uint32_t)(r * inner) : kOutside;
+      const uint32_t row = q >= 0 ? 2u * (uint32_t)(q * inner) : kOutside;
       const rsrc_t rs = s == 0 ? r_hsh : r_h;
 #pragma unroll
       for (int s4 = 0; s4 < kMaxISteps; ++s4) {
@@ -564,48 +580,44 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         st[s4] = ld_after16(rs, ks < nk ? row + 2u * (uint32_t)(32 * ks + kq) : kOutside);
       }
     };
-    auto compute = [&](u32x4 (&sa)[kMaxISteps], u32x4 (&sb)[kMaxISteps], int tok, int s) {
-      f32x4 d = zf4;
-#pragma unroll
-      for (int s4 = 0; s4 < kMaxISteps; ++s4) d = mfma16(sa[s4], sb[s4], d);
-      if (s < NS && nrows > 0) {
-        // The lane holds rows 4 (lane >> 4) + i of column m: accumulator half
-        // hl = lane >> 5; only columns of the same half are products (the
-        // lane's own column is then the one it loaded: same half, same pm).
-        const int hl = lane >> 5;
-        const bool use = hl == hm && tok >= 0;
-        // The two halves may hold the same token: half 0 first, then half 1.
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-          if (use && hl == pass) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int rr = 4 * ((lane >> 4) & 1) + i;
-              if (rr < nrows) s_acc[wave][rr][tok] += d[i];
-            }
-          }
-        }
-      }
+    // Two accumulators (even and odd k-steps) halve the MFMA dependency chain.
+    f32x4 acc0 = zf4, acc1 = zf4;
+    static_assert(kMaxISteps == 4, "compute() below takes four k-steps");
+    auto compute = [&](u32x4 (&sa)[kMaxISteps], u32x4 (&sb)[kMaxISteps]) {
+      acc0 = mfma16(sa[0], sb[0], acc0);
+      acc1 = mfma16(sa[1], sb[1], acc1);
+      acc0 = mfma16(sa[2], sb[2], acc0);
+      acc1 = mfma16(sa[3], sb[3], acc1);
     };
     static_assert(kCDepth == 6, "the loop below is unrolled for six stages");
 #pragma unroll
-    for (int s = 0; s < kCDepth; ++s) issue_b(cb[s], s, crow_h[s]);
-    for (int g0 = 0; g0 < NS; g0 += kCDepth) {
+    for (int s = 0; s < kCDepth; ++s) issue_b(cb[s], s, q0[s]);
+    if (NS <= kCDepth) {
+      // Every stage is already in flight (one or a few tokens).
 #pragma unroll
-      for (int s = 0; s < kCDepth; ++s) {
-        compute(ca[s], cb[s], ctok[s], g0 + s);
-        const int sn = g0 + s + kCDepth;
-        issue_a(ca[s], sn);
-        int tok = 0;
-        const int r = column(sn, hm, pm, &tok);
-        ctok[s] = r >= 0 ? tok : -1;
-        issue_b(cb[s], sn, r);
+      for (int s = 0; s < kCDepth; ++s) compute(ca[s], cb[s]);
+    } else {
+      for (int g0 = 0; g0 < NS; g0 += kCDepth) {
+#pragma unroll
+        for (int s = 0; s < kCDepth; ++s) {
+          compute(ca[s], cb[s]);
+          const int sn = g0 + s + kCDepth;
+          issue_a(ca[s], sn);
+          issue_b(cb[s], sn, cq(sn));
+        }
       }
     }
+    // The four waves' partial tiles, summed in a fixed order.  Element
+    // (i, j) of a tile is component i % 4 of lane 16 (i / 4) + j.
+    s_red[0][wave][lane] = acc0 + acc1;
     __syncthreads();
     if (tid < nrows * T) {
       const int rr = tid / T, t = tid - rr * T;
-      const float v = (s_acc[0][rr][t] + s_acc[1][rr][t]) + (s_acc[2][rr][t] + s_acc[3][rr][t]);
+      auto el = [&](int i, int j) {
+        const int l = 16 * (i >> 2) + j, c = i & 3;
+        return (s_red[0][0][l][c] + s_red[0][1][l][c]) + (s_red[0][2][l][c] + s_red[0][3][l][c]);
+      };
+      const float v = split_tok ? (t < 8 ? el(rr, t) : el(8 + rr, t)) : el(rr, t) + el(8 + rr, 8 + t);
       a.out[(size_t)t * H + row0 + rr] = (bf16_t)f32_to_bf16(v);
     }
   }
