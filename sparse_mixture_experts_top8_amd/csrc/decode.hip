@@ -502,10 +502,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     static_assert(kBDepth == 2, "the loop below is unrolled for two stages");
     issue(wa[0], 0);
     issue(wa[1], 1);
-    // The first down-projection stages do not depend on h: request them now,
-    // behind the first gate/up stages, so that they stream during phase B.
-#pragma unroll
-    for (int s = 0; s < kCDepth; ++s) issue_a(ca[s], s);
     // Phase C's B operands: for every stage and tile column the row of h
     // (routed: the pair of that expert and token) or of h_sh (stage 0), or -1.
     // Read after the hand-off barrier.
@@ -526,7 +522,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
       s_cq[i] = q;
     }
-    for (int i = 0; i < nmine; i += 2) {
+    // The first down-projection stages do not depend on h and are needed
+    // only after the hand-off: they are requested once this workgroup's first
+    // gate/up block has arrived, so that they do not compete with the gate/up
+    // streams that everything waits for.
+    compute(wa[0], 0);
+#pragma unroll
+    for (int s = 0; s < kCDepth; ++s) issue_a(ca[s], s);
+    issue(wa[0], 2);
+    compute(wa[1], 1);
+    issue(wa[1], 3);
+    for (int i = 2; i < nmine; i += 2) {
       compute(wa[0], i);
       issue(wa[0], i + 2);
       compute(wa[1], i + 1);
