@@ -325,7 +325,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int t = wave + kWaves * j;
-        if (t < T && lane < K) { s_tidx[t * K + lane] = ix[j]; s_tw[t * K + lane] = wv[j]; }
+        if (t < T && lane < K) {
+          s_tidx[t * K + lane] = ix[j];
+          s_tw[t * K + lane] = wv[j];
+          atomicOr(&s_mask[ix[j]], 1u << t);
+        }
       }
     };
     if (wave < T) {
@@ -337,12 +341,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   // ---------------- phase L: per-expert pair lists in LDS ----------------
-  // Token masks per expert, then offsets and the touched list (ascending
-  // expert) from one scan (low half: pair counts, high half: touched flags),
-  // then each pair's slot: its expert's offset plus the number of earlier
-  // tokens with that expert.
-  for (int q = tid; q < TK; q += kThreads) atomicOr(&s_mask[s_tidx[q]], 1u << (q / K));
-  __syncthreads();
+  // From the token masks per expert (set with the selections), wave 0 forms
+  // the offsets and the touched list (ascending expert) from one scan (low
+  // half: pair counts, high half: touched flags), then each pair's slot: its
+  // expert's offset plus the number of earlier tokens with that expert.
   if (wave == 0) {
     // Second scan: touched flags per token group (tokens 0-7 low half, 8-15
     // high half) for phase C with T > 8.
@@ -373,11 +375,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       gx += g4[j];
     }
     if (lane == 63) { s_off[E] = incl & 0xFFFF; s_U = incl >> 16; s_U01 = gincl; }
-  }
-  __syncthreads();
-  for (int q = tid; q < TK; q += kThreads) {
-    const int e = s_tidx[q], t = q / K;
-    s_list[s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u))] = q;
+    // The wave's own LDS writes above are visible to its reads below.
+    for (int q = lane; q < TK; q += kWave) {
+      const int e = s_tidx[q], t = q / K;
+      s_list[s_off[e] + __popc(s_mask[e] & ((1u << t) - 1u))] = q;
+    }
   }
   __syncthreads();
 
