@@ -20,7 +20,8 @@
 // partial sums.  Small batches split H into up to H/64 slices so that the
 // launch still spans the chip (a 64-token batch would otherwise be two
 // workgroups each reading the whole router).  router_select_kernel: one
-// workgroup per 32 tokens sums the slices in a fixed order and selects.
+// workgroup of 16 waves per 32 tokens sums the slices in a fixed order and
+// selects, two tokens per wave.
 #include "kernels.hpp"
 
 namespace moe {
@@ -121,64 +122,65 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
   }
 }
 
-// One workgroup per 32 tokens.  First all threads sum the slices of the
-// tile's partial rows in a fixed order (eight slices' loads in flight at a
-// time) into LDS; then each wave selects for eight tokens, in two interleaved
-// groups of four: top-K, weights, gate, block histogram.
-__global__ __launch_bounds__(256) void router_select_kernel(LayerArgs L, int T, int ksplit,
-                                                            const float* __restrict__ part, Work w,
-                                                            float* __restrict__ logits_out) {
+// One workgroup of 16 waves per 32 tokens.  First all threads sum the slices
+// of the tile's partial rows in a fixed order (every slice of an item in
+// flight at once) into LDS; then each wave selects for two tokens: top-K,
+// weights, gate, block histogram.
+constexpr int kSelWaves = 16;
+constexpr int kMaxSlices = 16;
+static_assert(kSelWaves * 2 == kTok, "two tokens per wave");
+
+__global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs L, int T, int ksplit,
+                                                                      const float* __restrict__ part, Work w,
+                                                                      float* __restrict__ logits_out) {
   __shared__ __attribute__((aligned(16))) float s_lg[kTok][kMaxRouterCols];
   __shared__ int hist[256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int E = L.E, K = L.K, Ep = router_cols(E), c4n = Ep / 4;
   const int t0 = blockIdx.x * kTok;
-  hist[tid] = 0;
-  for (int idx = tid; idx < kTok * c4n; idx += 256) {
+  if (tid < 256) hist[tid] = 0;
+  for (int idx = tid; idx < kTok * c4n; idx += kSelWaves * 64) {
     const int tl = idx / c4n, c4 = idx - tl * c4n;
     const float* src = part + (size_t)min(t0 + tl, T - 1) * Ep + 4 * c4;
+    u32x4 q[kMaxSlices];
+#pragma unroll
+    for (int i = 0; i < kMaxSlices; ++i)
+      if (i < ksplit) q[i] = ld16(src + (size_t)i * T * Ep);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ksplit; s0 += 8) {
-      u32x4 q[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = ld16(src + (size_t)min(s0 + i, ksplit - 1) * T * Ep);
+    for (int i = 0; i < kMaxSlices; ++i)
+      if (i < ksplit)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (s0 + i < ksplit)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] += __uint_as_float(q[i][c]);
-    }
+        for (int c = 0; c < 4; ++c) v[c] += __uint_as_float(q[i][c]);
     *reinterpret_cast<f32x4*>(&s_lg[tl][4 * c4]) = v;
   }
   __syncthreads();
-  for (int g = 0; g < 2; ++g) {
-    float lv[4][4];
-    int tt[4];
+  float lv[2][4];
+  int tt[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = wave * 8 + g * 4 + j;
-      tt[j] = t0 + tl;
-      // Columns 4 lane .. 4 lane + 3; past E they are outside the top-K's
-      // valid range (reads stay inside the padded row).
+  for (int j = 0; j < 2; ++j) {
+    const int tl = 2 * wave + j;
+    tt[j] = t0 + tl;
+    // Columns 4 lane .. 4 lane + 3; past E they are outside the top-K's valid
+    // range (reads stay inside the padded row).
 #pragma unroll
-      for (int c = 0; c < 4; ++c) lv[j][c] = s_lg[tl][min(4 * lane + c, kMaxRouterCols - 1)];
-      if (tt[j] < T && lane == 0) w.gate_s[tt[j]] = sigmoidf_(s_lg[tl][E]);
-      if (logits_out && tt[j] < T) {
+    for (int c = 0; c < 4; ++c) lv[j][c] = s_lg[tl][min(4 * lane + c, kMaxRouterCols - 1)];
+    if (tt[j] < T && lane == 0) w.gate_s[tt[j]] = sigmoidf_(s_lg[tl][E]);
+    if (logits_out && tt[j] < T) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (4 * lane + c < E) logits_out[(size_t)tt[j] * E + 4 * lane + c] = lv[j][c];
-      }
+      for (int c = 0; c < 4; ++c)
+        if (4 * lane + c < E) logits_out[(size_t)tt[j] * E + 4 * lane + c] = lv[j][c];
     }
-    int ix[4];
-    float wv[4];
-    topk_select<4>(lv, E, K, lane, ix, wv);
+  }
+  int ix[2];
+  float wv[2];
+  topk_select<2>(lv, E, K, lane, ix, wv);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (tt[j] < T && lane < K) {
-        w.topk_idx[(size_t)tt[j] * K + lane] = ix[j];
-        w.topk_w[(size_t)tt[j] * K + lane] = wv[j];
-        atomicAdd(&hist[ix[j]], 1);
-      }
+  for (int j = 0; j < 2; ++j) {
+    if (tt[j] < T && lane < K) {
+      w.topk_idx[(size_t)tt[j] * K + lane] = ix[j];
+      w.topk_w[(size_t)tt[j] * K + lane] = wv[j];
+      atomicAdd(&hist[ix[j]], 1);
     }
   }
   __syncthreads();
@@ -200,8 +202,8 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
   hipLaunchKernelGGL(router_logits_kernel, dim3(nblk, ks), dim3(256), 0, s, L, x, T, ks, w.rlog);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_select_kernel, dim3(nblk), dim3(256), 0, s, L, T, ks, (const float*)w.rlog, w,
-                     logits_out);
+  hipLaunchKernelGGL(router_select_kernel, dim3(nblk), dim3(kSelWaves * 64), 0, s, L, T, ks, (const float*)w.rlog,
+                     w, logits_out);
   return hipGetLastError();
 }
 
