@@ -125,9 +125,112 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(LayerArgs L, int 
   }
 }
 
+// Batches of at most kSmallBlocks router blocks: the whole dispatch in one
+// workgroup.  Token masks per (block, expert) are built in LDS; an expert's
+// count in a block is its mask's population, the pair's rank among the
+// block's pairs of that expert is the population of the mask below its
+// token (tokens of a block are distinct per expert, and pair ids grow with
+// the token), so the slots equal those of the multi-kernel path.
+constexpr int kSmallBlocks = 64;
+constexpr int kSmallThreads = 1024;
+
+__global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs L, int T, Work w) {
+  __shared__ uint32_t s_mask[kSmallBlocks * 256];
+  __shared__ int s_base[kSmallBlocks * 256];
+  __shared__ int s_cnt[256], s_off[257], s_tgu[258], s_tdn[258];
+  __shared__ int wave_tot[kSmallThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = L.E, K = L.K, TK = T * K;
+  const int nblk = router_blocks(T);
+  for (int i = tid; i < nblk * E; i += kSmallThreads) s_mask[i] = 0u;
+  __syncthreads();
+  for (int q = tid; q < TK; q += kSmallThreads) {
+    const int t = q / K, b = t / kRouterTokens;
+    atomicOr(&s_mask[b * E + w.topk_idx[q]], 1u << (t - b * kRouterTokens));
+  }
+  __syncthreads();
+  // Per expert: exclusive prefix of its counts over the blocks.
+  if (tid < E) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      s_base[b * E + tid] = run;
+      run += __popc(s_mask[b * E + tid]);
+    }
+    s_cnt[tid] = run;
+  }
+  __syncthreads();
+  // Segment offsets and tile prefix sums (one wave per quantity, 256 experts
+  // as four per lane; group E is the shared expert with T rows).
+  if (wave < 3) {
+    int v[4], run = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      const int cnt = e < E ? s_cnt[e] : 0;
+      const int mt = (cnt + kGemmBM - 1) / kGemmBM;
+      v[j] = wave == 0 ? cnt : (wave == 1 ? mt * ((2 * L.I + kGemmBNW - 1) / kGemmBNW) : mt * (L.H / kGemmBNW));
+      run += v[j];
+    }
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += n;
+    }
+    int ex = incl - run;
+    int* dst = wave == 0 ? s_off : (wave == 1 ? s_tgu : s_tdn);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      if (e < E) dst[e] = ex;
+      ex += v[j];
+    }
+    if (lane == 63) {
+      const int mt = (T + kGemmBM - 1) / kGemmBM;
+      dst[E] = incl;
+      if (wave == 1) dst[E + 1] = incl + mt * ((2 * L.Is + kGemmBNW - 1) / kGemmBNW);
+      if (wave == 2) dst[E + 1] = incl + mt * (L.H / kGemmBNW);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += kSmallThreads) w.offsets[e] = s_off[e];
+  for (int g = tid; g <= E + 1; g += kSmallThreads) {
+    w.tiles_gu[g] = s_tgu[g];
+    w.tiles_dn[g] = s_tdn[g];
+  }
+  // Tile descriptors, one thread per group (column tile major).
+  if (tid <= E) {
+    const int g = tid;
+    const bool shared = g == E;
+    const int seg0 = shared ? 0 : s_off[g];
+    const int nrows = shared ? T : s_cnt[g];
+    const int mt = (nrows + kGemmBM - 1) / kGemmBM;
+    const int ngu = (2 * (shared ? L.Is : L.I) + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
+    int4* gu = w.tdesc_gu + s_tgu[g];
+    for (int nt = 0; nt < ngu; ++nt)
+      for (int mi = 0; mi < mt; ++mi) *gu++ = make_int4(g, seg0, nrows, mi | (nt << 16));
+    int4* dn = w.tdesc_dn + s_tdn[g];
+    for (int nt = 0; nt < ndn; ++nt)
+      for (int mi = 0; mi < mt; ++mi) *dn++ = make_int4(g, seg0, nrows, mi | (nt << 16));
+  }
+  // Scatter.
+  for (int q = tid; q < TK; q += kSmallThreads) {
+    const int t = q / K, b = t / kRouterTokens, e = w.topk_idx[q];
+    const uint32_t below = s_mask[b * E + e] & ((1u << (t - b * kRouterTokens)) - 1u);
+    const int slot = s_off[e] + s_base[b * E + e] + __popc(below);
+    w.perm[slot] = q;
+    w.slot_of[q] = slot;
+    w.slot_tok[slot] = t;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s) {
+  if (router_blocks(T) <= kSmallBlocks) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallThreads), 0, s, L, T, w);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.E), dim3(256), 0, s, L, T, w);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, L, T, w);
   hipLaunchKernelGGL(dispatch_tiles_kernel, dim3(L.E + 1), dim3(256), 0, s, L, T, w);
