@@ -284,23 +284,41 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
 }
 
 // out[t] = bf16( sum_k w[t, k] y[slot_of(t, k)] + gate[t] y[T*K + t] ), k in
-// order, fp32 sum.
+// order, fp32 sum.  The K + 1 row indices and scales are requested first,
+// then all K + 1 rows, so the loads overlap instead of forming a chain.
+constexpr int kMaxK = 8;
 __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int K, Work w, bf16_t* __restrict__ out) {
   const int per_tok = H >> 3;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)T * per_tok) return;
   const int t = (int)(idx / per_tok), c = (int)(idx % per_tok) * 8;
+  size_t row[kMaxK + 1];
+  float sc[kMaxK + 1];
+#pragma unroll
+  for (int k = 0; k <= kMaxK; ++k) {
+    if (k < K) {
+      row[k] = (size_t)w.slot_of[(size_t)t * K + k];
+      sc[k] = w.topk_w[(size_t)t * K + k];
+    } else {
+      row[k] = (size_t)T * K + t;
+      sc[k] = k == K ? w.gate_s[t] : 0.f;
+    }
+  }
+  u32x4 v[kMaxK + 1];
+#pragma unroll
+  for (int k = 0; k <= kMaxK; ++k)
+    if (k <= K) v[k] = ld16(w.y + row[k] * H + c);
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int k = 0; k <= K; ++k) {
-    const size_t row = k < K ? (size_t)w.slot_of[(size_t)t * K + k] : (size_t)T * K + t;
-    const float sc = k < K ? w.topk_w[(size_t)t * K + k] : w.gate_s[t];
-    const u32x4 v = ld16(w.y + row * H + c);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += sc * bf16_to_f32(v[j] & 0xFFFFu);
-      acc[2 * j + 1] += sc * bf16_to_f32(v[j] >> 16);
+  for (int k = 0; k <= kMaxK; ++k) {
+    if (k <= K) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += sc[k] * bf16_to_f32(v[k][j] & 0xFFFFu);
+        acc[2 * j + 1] += sc[k] * bf16_to_f32(v[k][j] >> 16);
+      }
     }
   }
   u32x4 o;
