@@ -13,63 +13,64 @@
 // the same quantity as a softmax over the K selected logits alone (the full
 // denominator cancels); the kernel computes the latter.
 //
-// Two kernels.  router_logits_kernel: one workgroup per (32-token tile, slice
-// of H); the shared gate row rides along as column E, so the E + 1 columns
+// Two kernels.  router_logits_kernel: one workgroup per (64-token tile, or
+// 32-token tile for small batches, slice of H); the shared gate row rides along as column E, so the E + 1 columns
 // are 17 MFMA column blocks of 16.  Each wave streams its column blocks' rows
-// and the tile's x rows through a four-step register pipeline and writes fp32
-// partial sums.  Small batches split H into up to H/64 slices so that the
-// launch still spans the chip (a 64-token batch would otherwise be two
-// workgroups each reading the whole router).  router_select_kernel: one
-// workgroup of 16 waves per 32 tokens sums the slices in a fixed order and
-// selects, two tokens per wave.
+// and the tile's x rows through a three-step register pipeline and writes
+// fp32 partial sums (one fp32 accumulator chain of at most H / 32 steps per
+// slice).  For large batches the router is read once per 64 tokens: its
+// re-reads through L2, not the arithmetic, set the kernel's pace.  Small batches split H into up
+// to H/64 slices so that the launch still spans the chip.
+// router_select_kernel: one workgroup of 16 waves per 32 tokens sums the
+// slices in a fixed order and selects, two tokens per wave.
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kTok = kRouterTokens;      // 32 tokens per tile
+constexpr int kTok = kRouterTokens;      // 32 tokens per select block
+constexpr int kSmallT = 256;             // up to this many tokens: 32-token logits tiles, else 64
 constexpr int kColBlocks = 5;            // column blocks per wave (17 for E = 256, plus the gate column)
-constexpr int kDepth = 4;                // k-steps in flight per wave
+constexpr int kDepth = 3;                // k-steps in flight per wave
 constexpr int kMaxRouterCols = 260;      // router_cols(256)
 
+// kTB 16-token blocks per workgroup.
+template <int kTB>
 __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
                                                             int ksplit, float* __restrict__ part) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * kTok, s = blockIdx.y;
+  const int t0 = blockIdx.x * 16 * kTB, s = blockIdx.y;
   const int H = L.H, E = L.E, Ep = router_cols(E);
   const int nsub = (E + 1 + 15) >> 4;               // column blocks incl. the gate column
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   const int klen = H / ksplit, kbeg = s * klen, nk = klen / 32;
 
-  // Operand rows of this lane: x rows of the two 16-token halves, weight rows
-  // of the wave's column blocks (rows past T or E + 1 repeat a valid row and
+  // Operand rows of this lane: x rows of the 16-token blocks, weight rows of
+  // the wave's column blocks (rows past T or E + 1 repeat a valid row and
   // their outputs are dropped).
-  const bf16_t* arow[2];
+  const bf16_t* arow[kTB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) arow[i] = x + (size_t)min(t0 + 16 * i + r16, T - 1) * H + kbeg + kq;
+  for (int i = 0; i < kTB; ++i) arow[i] = x + (size_t)min(t0 + 16 * i + r16, T - 1) * H + kbeg + kq;
   const bf16_t* brow[kColBlocks];
 #pragma unroll
   for (int jj = 0; jj < kColBlocks; ++jj) {
     const int e = min(16 * (wave + 4 * jj) + r16, E);
     brow[jj] = (e < E ? L.router_w + (size_t)e * H : L.sh_expert_gate) + kbeg + kq;
   }
-  f32x4 acc[2][kColBlocks], tot[2][kColBlocks];
+  f32x4 acc[kTB][kColBlocks];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kTB; ++i)
 #pragma unroll
-    for (int jj = 0; jj < kColBlocks; ++jj) {
-      acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-      tot[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int jj = 0; jj < kColBlocks; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Ring of kDepth k-steps; loads of k-steps past the slice repeat its last
   // step (always in bounds) and are not used.
-  u32x4 ra[kDepth][2], rb[kDepth][kColBlocks];
+  u32x4 ra[kDepth][kTB], rb[kDepth][kColBlocks];
   auto issue = [&](int st, int ks) {
     const int k = 32 * min(ks, nk - 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ra[st][i] = ld16(arow[i] + k);
+    for (int i = 0; i < kTB; ++i) ra[st][i] = ld16(arow[i] + k);
 #pragma unroll
     for (int jj = 0; jj < kColBlocks; ++jj) rb[st][jj] = ld16(brow[jj] + k);
   };
@@ -84,22 +85,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
         for (int jj = 0; jj < kColBlocks; ++jj) {
           if (wave + 4 * jj < nsub) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < kTB; ++i)
               acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[st][i]), as_bf16x8(rb[st][jj]),
                                                                    acc[i][jj], 0, 0, 0);
           }
-        }
-        // Every 256 elements the running sums fold into a second fp32 total,
-        // which keeps the rounding error of the long dot product near that of
-        // a pairwise sum.
-        if ((ks & 7) == 7 || ks == nk - 1) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int jj = 0; jj < kColBlocks; ++jj) {
-              tot[i][jj] += acc[i][jj];
-              acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
         }
       }
       issue(st, ks + kDepth);
@@ -112,11 +101,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
     const int e = 16 * (wave + 4 * jj) + r16;
     if (wave + 4 * jj < nsub && e <= E) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kTB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + 16 * i + 4 * (lane >> 4) + r;
-          if (t < T) out[(size_t)t * Ep + e] = tot[i][jj][r];
+          if (t < T) out[(size_t)t * Ep + e] = acc[i][jj][r];
         }
     }
   }
@@ -189,8 +178,10 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs
 
 }  // namespace
 
+static int logits_tile(int T) { return T <= kSmallT ? 32 : 64; }
+
 int router_ksplit(int T, int H) {
-  const int ntiles = router_blocks(T);
+  const int ntiles = (T + logits_tile(T) - 1) / logits_tile(T);
   int s = 1;
   while (2 * s <= H / 64 && 2 * s <= 16 && ntiles * s < 256) s *= 2;
   return s;
@@ -198,12 +189,16 @@ int router_ksplit(int T, int H) {
 
 hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
                          float* logits_out, hipStream_t s) {
-  const int nblk = router_blocks(T), ks = router_ksplit(T, L.H);
-  hipLaunchKernelGGL(router_logits_kernel, dim3(nblk, ks), dim3(256), 0, s, L, x, T, ks, w.rlog);
+  const int ks = router_ksplit(T, L.H), tile = logits_tile(T);
+  const dim3 grid((T + tile - 1) / tile, ks);
+  if (tile == 32)
+    hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog);
+  else
+    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_select_kernel, dim3(nblk), dim3(kSelWaves * 64), 0, s, L, T, ks, (const float*)w.rlog,
-                     w, logits_out);
+  hipLaunchKernelGGL(router_select_kernel, dim3(router_blocks(T)), dim3(kSelWaves * 64), 0, s, L, T, ks,
+                     (const float*)w.rlog, w, logits_out);
   return hipGetLastError();
 }
 
