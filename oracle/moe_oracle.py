@@ -34,7 +34,9 @@ notes of this repository):
 * SiLU(z) = z * sigmoid(z), sigmoid(z) = 1 / (1 + exp(-z));
 * the shared-expert gate scales only the shared expert's output;
 * no capacity limit: every (token, expert) pair is computed;
-* the layer output excludes the residual and any norm.
+* the layer output excludes the residual and any norm;
+* the load-balance statistic is E * sum_e f_e * P_e (slot fraction times
+  mean full-softmax probability), the page giving no formula.
 
 Inputs are bf16 bit patterns (uint16 arrays); parameters are passed as a
 mapping keyed by the model page's member names: ``gate.weight``,
@@ -267,6 +269,35 @@ def forward_dense(x: np.ndarray, params: dict, K: int) -> np.ndarray:
     for e in range(E):
         out += w[:, e:e + 1] * routed_expert(X, params, e, I)
     return out + shared_gate(x, params)[:, None] * shared_expert(X, params)
+
+
+# ---------------------------------------------------------------------------
+# Load-balance statistic (section "MoE FFN: 256 Experts", Load Balancing).
+# ---------------------------------------------------------------------------
+
+def load_balance(x: np.ndarray, params: dict, K: int) -> dict:
+    """Forward-only load-balance statistic of one batch.
+
+    The page names an auxiliary loss (coefficient 0.001) that penalises uneven
+    use of the experts, without a formula.  Reading taken here: the fraction
+    of the T*K routing slots that go to expert e, f_e = counts[e] / (T K),
+    times the batch mean of its full-softmax router probability,
+    P_e = (1/T) sum_t p[t, e], summed over the experts and scaled by E:
+
+        lb = E * sum_e f_e * P_e
+
+    which is 1 when both are uniform and grows as routing concentrates (the
+    training loss would be 0.001 * lb; no gradient is formed here).
+    """
+    logits = router_logits(x, params["gate.weight"])
+    topk_idx, _ = select_topk(logits, K)
+    T, E = logits.shape
+    counts = np.bincount(topk_idx.reshape(-1).astype(np.int64), minlength=E)
+    f = counts / float(T * K)
+    P = softmax_rows(logits).mean(axis=0)
+    return {"counts": counts.astype(np.int32), "fraction": f, "mean_prob": P,
+            "lb": float(E * np.sum(f * P)), "logits": logits, "topk_idx": topk_idx,
+            "tie": tie_flags(logits, K)}
 
 
 def expert_param_count(H: int, I: int) -> int:

@@ -375,3 +375,77 @@ def test_zipf_workload_is_skewed():
     assert load.sum() == wl.T * wl.dims.K
     assert load.max() >= 10 * mean
     assert load.max() <= 0.5 * wl.T          # an expert cannot win more than about half the tokens
+
+
+# ---------------------------------------------------------------------------
+# Load-balance statistic.
+# ---------------------------------------------------------------------------
+
+def _lb_brute(x, layer, K):
+    """The statistic from its definition with Python loops and the math module."""
+    X = O.bf16_to_f64(x)
+    W = O.bf16_to_f64(layer["gate.weight"])
+    T, E = X.shape[0], W.shape[0]
+    counts = [0] * E
+    psum = [0.0] * E
+    for t in range(T):
+        l = [sum(X[t, h] * W[e, h] for h in range(X.shape[1])) for e in range(E)]
+        order = sorted(range(E), key=lambda e: (-l[e], e))
+        for e in order[:K]:
+            counts[e] += 1
+        m = max(l)
+        z = [math.exp(v - m) for v in l]
+        s = sum(z)
+        for e in range(E):
+            psum[e] += z[e] / s
+    lb = E * sum((counts[e] / (T * K)) * (psum[e] / T) for e in range(E))
+    return counts, [p / T for p in psum], lb
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_load_balance_brute_force(seed):
+    d = mi.Dims(H=16, E=8, K=3, I=8, Is=8)
+    layer = _random_layer(d, 300 + seed, std=0.5)
+    x = mi.make_x(d, 6, 310 + seed)
+    r = O.load_balance(x, layer, d.K)
+    counts, P, lb = _lb_brute(x, layer, d.K)
+    assert list(r["counts"]) == counts
+    np.testing.assert_allclose(r["mean_prob"], P, rtol=1e-12, atol=1e-15)
+    assert abs(r["lb"] - lb) <= 1e-12 * lb
+
+
+def test_load_balance_closed_forms():
+    d = mi.TOY
+    layer = _random_layer(d, 320)
+    # x = 0: every logit is 0, so P_e = 1/E and experts 0..K-1 take every slot:
+    # lb = E * K * (1/K) * (1/E) = 1 exactly.
+    r0 = O.load_balance(np.zeros((11, d.H), np.uint16), layer, d.K)
+    assert list(r0["counts"][:d.K]) == [11] * d.K and r0["counts"][d.K:].sum() == 0
+    np.testing.assert_allclose(r0["mean_prob"], 1.0 / d.E, rtol=0, atol=1e-15)
+    assert abs(r0["lb"] - 1.0) < 1e-14
+    # Fractions and mean probabilities are distributions.
+    x = mi.make_x(d, 40, 321)
+    r = O.load_balance(x, layer, d.K)
+    assert abs(r["fraction"].sum() - 1.0) < 1e-12 and abs(r["mean_prob"].sum() - 1.0) < 1e-12
+    assert r["counts"].sum() == 40 * d.K
+    # Every token sends its K slots to the same experts S: lb = (E / K) P(S),
+    # P(S) the batch-mean probability mass of S.  Router rows 0..K-1 get a
+    # large copy of one row, so those K experts win for inputs that align with it.
+    g = O.bf16_to_f64(layer["gate.weight"]).copy()
+    g[: d.K] = 8.0 * g[0] + np.arange(d.K)[:, None] * 1e-3 * np.sign(g[0])
+    lay2 = dict(layer, **{"gate.weight": _bits(g)})
+    xa = _bits(np.tile(np.sign(g[0]), (7, 1)) * (1.0 + 0.1 * np.arange(7))[:, None])
+    r2 = O.load_balance(xa, lay2, d.K)
+    assert set(np.nonzero(r2["counts"])[0]) == set(range(d.K))
+    assert abs(r2["lb"] - d.E / d.K * r2["mean_prob"][: d.K].sum()) < 1e-12
+
+
+def test_load_balance_token_permutation():
+    d = mi.TOY
+    layer = _random_layer(d, 330)
+    x = mi.make_x(d, 25, 331)
+    r = O.load_balance(x, layer, d.K)
+    rp = O.load_balance(x[np.random.default_rng(3).permutation(25)], layer, d.K)
+    assert np.array_equal(r["counts"], rp["counts"])
+    np.testing.assert_allclose(rp["mean_prob"], r["mean_prob"], rtol=1e-12)
+    assert abs(rp["lb"] - r["lb"]) < 1e-12 * r["lb"]
