@@ -228,6 +228,21 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / steps
 
+    # Load-balance statistic of the same batches (moe_load_balance: router,
+    # dispatch and the statistic), timed outside the step.
+    lb_steps = min(steps, 200)
+    lb_out = [moe.load_balance(xs[l], layers[l], ws=ws) for l in range(nlayers)]
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(lb_steps):
+        l = i % nlayers
+        moe.load_balance(xs[l], layers[l], ws=ws)
+    end.record()
+    torch.cuda.synchronize()
+    load_balance = {"us_per_call": round(start.elapsed_time(end) / lb_steps * 1e3, 2),
+                    "lb": round(float(np.mean([float(r["lb"].item()) for r in lb_out])), 6),
+                    "definition": "E * sum_e f_e * P_e (slot fraction x mean full-softmax probability)"}
+
     # Kernel attribution: the same steps again, each recording six events at
     # its phase boundaries on the same stream (the fused decode path records
     # its single kernel between events 0 and 1).
@@ -299,6 +314,7 @@ def main():
                    "device": prop.name, "cus": prop.multi_processor_count},
         "roofline": roof,
         "layer": layer_stats,
+        "load_balance": load_balance,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

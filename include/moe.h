@@ -107,6 +107,24 @@ int moe_route(const moe_layer_t *L, const void *x, int64_t T,
               float *shared_gate, float *logits,
               void *ws, size_t ws_bytes, void *stream);
 
+/* Forward-only router load-balance statistic of a batch ("Qwen3.6-35B-A3B —
+ * Architecture Overview", section "MoE FFN: 256 Experts", Load Balancing:
+ * an auxiliary loss penalises uneven expert use; the page gives no formula).
+ * With f_e = counts[e] / (T K), the share of the T*K routing slots that expert
+ * e receives, and P_e = (1/T) sum_t softmax(logits[t])[e], the batch-mean
+ * full-softmax probability:
+ *   lb        fp32 [1]   E * sum_e f_e * P_e  (1 when both are uniform; the
+ *                        training loss would be 0.001 * lb)
+ *   mean_prob fp32 [E] or NULL   P_e
+ *   counts    int32 [E] or NULL  pairs routed to each expert
+ * Device pointers, 4-byte aligned; x bf16 [T, H] and the workspace (size from
+ * moe_workspace_bytes) 16-byte aligned.  Uses the same router, top-K and
+ * dispatch kernels as moe_forward for T > 16 at any T; sums are in a fixed
+ * order, so repeated calls give identical results.  T = 0 is a successful
+ * no-op.  Errors as moe_route. */
+int moe_load_balance(const moe_layer_t *L, const void *x, int64_t T, float *lb, float *mean_prob,
+                     int32_t *counts, void *ws, size_t ws_bytes, void *stream);
+
 /* The whole layer: out bf16 [T, H] (round to nearest even from an fp32
  * accumulation).  x and out must not overlap.  T = 0 is a successful no-op. */
 int moe_forward(const moe_layer_t *L, const void *x, int64_t T, void *out,

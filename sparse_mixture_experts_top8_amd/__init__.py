@@ -140,3 +140,22 @@ def route(x: torch.Tensor, layer: MoeLayer, ws: torch.Tensor | None = None, stre
     if rc != 0:
         raise MoeError(rc, "moe_route")
     return r
+
+
+def load_balance(x: torch.Tensor, layer: MoeLayer, ws: torch.Tensor | None = None, stream=None) -> dict:
+    """Router load-balance statistic (moe_load_balance); returns device tensors
+    lb [1], mean_prob [E] and counts [E]."""
+    _check_x(x, layer)
+    T, dev = x.shape[0], x.device
+    r = {
+        "lb": torch.empty(1, dtype=torch.float32, device=dev),
+        "mean_prob": torch.empty(layer.E, dtype=torch.float32, device=dev),
+        "counts": torch.empty(layer.E, dtype=torch.int32, device=dev),
+    }
+    if ws is None:
+        ws = layer.workspace(T, dev)
+    rc = lib.moe_load_balance(layer.desc, _ptr(x), T, _ptr(r["lb"]), _ptr(r["mean_prob"]), _ptr(r["counts"]),
+                              _ptr(ws), ws.numel(), _stream_handle(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_load_balance")
+    return r

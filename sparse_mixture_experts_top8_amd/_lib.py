@@ -21,7 +21,7 @@ MOE_ERR_DEVICE = 5
 MOE_ERR_LAUNCH = 6
 
 # Exported entry points, as include/moe.h declares them.
-EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_forward",
+EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_load_balance", "moe_forward",
            "moe_forward_traced", "moe_strerror", "moe_last_error")
 
 
@@ -61,6 +61,8 @@ def _load():
     lib.moe_validate.restype = ctypes.c_int
     lib.moe_route.argtypes = [L, P, ctypes.c_int64, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_route.restype = ctypes.c_int
+    lib.moe_load_balance.argtypes = [L, P, ctypes.c_int64, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_load_balance.restype = ctypes.c_int
     lib.moe_forward.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P]
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward_traced.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P, P]

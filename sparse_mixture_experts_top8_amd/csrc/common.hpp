@@ -66,6 +66,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
+// Sum of a float over the wave, in every lane, in a fixed order: four DPP
+// steps inside each 16-lane row (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror), then the four row sums.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Top-K (K <= 8) of NT tokens by one wave (independent chains, interleaved),
 // from each lane's four logits of experts 4 lane + c: order by descending
 // logit, ties to the lower expert index; lane k < K receives the k-th index
@@ -169,6 +188,7 @@ struct Work {
   bf16_t* h;           // [T*K, I]
   bf16_t* h_sh;        // [T, Is]
   bf16_t* y;           // [T*K + T, H]  weighted expert outputs, routed slots then shared rows
+  float* psum;         // [nblk * E]  per router block: sum over its tokens of each expert's softmax probability
 };
 
 }  // namespace moe

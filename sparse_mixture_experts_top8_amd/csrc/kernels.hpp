@@ -63,8 +63,14 @@ int decode_max_grid(int num_cus);
 // rows (16-row tiles).
 bool decode_fits(int H, int E, int Is, int grid);
 
+// psum_out (optional): per router block, the sum over its tokens of every
+// expert's full-softmax probability (the load-balance statistic's input).
 hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
-                         float* logits_out, hipStream_t s);
+                         float* logits_out, hipStream_t s, float* psum_out = nullptr);
+// Load-balance statistic from the block probability sums and the dispatch
+// offsets: lb [1], mean_prob [E] (optional), counts [E] (optional).
+hipError_t launch_load_balance(const LayerArgs& L, int T, const Work& w, float* lb, float* mean_prob,
+                               int32_t* counts, hipStream_t s);
 hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s);
 hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
                           int num_cus, hipStream_t s);

@@ -83,6 +83,7 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   c.w.h = (bf16_t*)take(tk * I * 2);
   c.w.h_sh = (bf16_t*)take(t * Is * 2);
   c.w.y = (bf16_t*)take((tk + t) * H * 2);
+  c.w.psum = (float*)take(nblk * E * 4);
   c.bytes = off;
   return c;
 }
@@ -298,6 +299,34 @@ int moe_route(const moe_layer_t* L, const void* x, int64_t T, int32_t* topk_idx,
   hipStream_t s = (hipStream_t)stream;
   if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, (int)T, w, logits, s), "router")) != MOE_OK) return rc;
   return launch_status(moe::launch_dispatch(a, (int)T, w, s), "dispatch");
+}
+
+int moe_load_balance(const moe_layer_t* L, const void* x, int64_t T, float* lb, float* mean_prob,
+                     int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(L, T);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_weights(L)) != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !lb || !ws) return fail(MOE_ERR_NULL, "x, lb and workspace are required");
+  const void* ptrs[5] = {x, ws, lb, mean_prob, counts};
+  for (int i = 0; i < 2; ++i)
+    if (!aligned16(ptrs[i])) return fail(MOE_ERR_ALIGN, "x or the workspace is not 16-byte aligned");
+  for (int i = 2; i < 5; ++i)
+    if (ptrs[i] && ((uintptr_t)ptrs[i] & 3u)) return fail(MOE_ERR_ALIGN, "lb, mean_prob and counts need 4-byte alignment");
+  const size_t need = workspace_need(L, T);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T = %lld", ws_bytes, need, (long long)T);
+  int cus = 0, dgrid = 0;
+  if ((rc = device_check(&cus, &dgrid)) != MOE_OK) return rc;
+  // Always the grouped path's router and dispatch (any T).
+  const moe::Work w = carve(L, T, (char*)ws).w;
+  const moe::LayerArgs a = layer_args(L);
+  hipStream_t s = (hipStream_t)stream;
+  const int t = (int)T;
+  if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, t, w, nullptr, s, w.psum), "router")) != MOE_OK)
+    return rc;
+  if ((rc = launch_status(moe::launch_dispatch(a, t, w, s), "dispatch")) != MOE_OK) return rc;
+  return launch_status(moe::launch_load_balance(a, t, w, lb, mean_prob, counts, s), "load balance");
 }
 
 int moe_forward_traced(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws,

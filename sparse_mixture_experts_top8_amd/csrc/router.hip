@@ -121,7 +121,8 @@ static_assert(kSelWaves * 2 == kTok, "two tokens per wave");
 
 __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs L, int T, int ksplit,
                                                                       const float* __restrict__ part, Work w,
-                                                                      float* __restrict__ logits_out) {
+                                                                      float* __restrict__ logits_out,
+                                                                      float* __restrict__ psum_out) {
   __shared__ __attribute__((aligned(16))) float s_lg[kTok][kMaxRouterCols];
   __shared__ int hist[256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -172,8 +173,80 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs
       atomicAdd(&hist[ix[j]], 1);
     }
   }
+  if (psum_out) {
+    // Load-balance input: each token's full softmax over the E experts
+    // (written over its logits in LDS), then per expert the sum over the
+    // block's tokens in token order.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t mk = 0u;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mk = max(mk, 4 * lane + c < E ? logit_key(lv[j][c]) : 0u);
+      const float mx = key_logit(wave_max_u32(mk));
+      float z[4], zs = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        z[c] = 4 * lane + c < E ? __expf(lv[j][c] - mx) : 0.f;
+        zs += z[c];
+      }
+      const float inv = 1.0f / wave_sum_f32(zs);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (4 * lane + c < E) s_lg[2 * wave + j][4 * lane + c] = z[c] * inv;
+    }
+  }
   __syncthreads();
   if (tid < E) w.blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
+  if (psum_out && tid < E) {
+    float acc = 0.f;
+    const int nt = min(kTok, T - t0);
+    for (int tl = 0; tl < nt; ++tl) acc += s_lg[tl][tid];
+    psum_out[(size_t)blockIdx.x * E + tid] = acc;
+  }
+}
+
+// Load-balance statistic, one workgroup of 1024 threads: per expert, four
+// threads sum the block probability sums of four contiguous block ranges
+// (eight loads in flight each), the ranges are added in order, the pair count
+// comes from the segment offsets; lb = E * sum_e (count_e / (T K)) *
+// (psum_e / T), summed in double over the experts in a fixed tree order.
+__global__ __launch_bounds__(1024) void load_balance_kernel(LayerArgs L, int T, Work w, float* __restrict__ lb,
+                                                            float* __restrict__ mean_prob,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ float s_part[4][256];
+  __shared__ double s_term[256];
+  const int tid = threadIdx.x, e = tid & 255, part = tid >> 8, E = L.E, K = L.K;
+  const int nblk = router_blocks(T);
+  const int per = (nblk + 3) >> 2, b0 = part * per, b1 = min(nblk, b0 + per);
+  float ps = 0.f;
+  if (e < E) {
+    for (int b = b0; b < b1; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = b + i < b1 ? w.psum[(size_t)(b + i) * E + e] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ps += v[i];
+    }
+  }
+  s_part[part][e] = ps;
+  __syncthreads();
+  if (tid < 256) {
+    double term = 0.0;
+    if (e < E) {
+      const float tot = (s_part[0][e] + s_part[1][e]) + (s_part[2][e] + s_part[3][e]);
+      const int cnt = w.offsets[e + 1] - w.offsets[e];
+      if (mean_prob) mean_prob[e] = tot / (float)T;
+      if (counts) counts[e] = cnt;
+      term = (double)cnt * (double)tot;
+    }
+    s_term[e] = term;
+  }
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) s_term[tid] += s_term[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) *lb = (float)(s_term[0] * (double)E / ((double)T * K * (double)T));
 }
 
 }  // namespace
@@ -188,7 +261,7 @@ int router_ksplit(int T, int H) {
 }
 
 hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
-                         float* logits_out, hipStream_t s) {
+                         float* logits_out, hipStream_t s, float* psum_out) {
   const int ks = router_ksplit(T, L.H), tile = logits_tile(T);
   const dim3 grid((T + tile - 1) / tile, ks);
   if (tile == 32)
@@ -198,7 +271,13 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(router_select_kernel, dim3(router_blocks(T)), dim3(kSelWaves * 64), 0, s, L, T, ks,
-                     (const float*)w.rlog, w, logits_out);
+                     (const float*)w.rlog, w, logits_out, psum_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_load_balance(const LayerArgs& L, int T, const Work& w, float* lb, float* mean_prob,
+                               int32_t* counts, hipStream_t s) {
+  hipLaunchKernelGGL(load_balance_kernel, dim3(1), dim3(1024), 0, s, L, T, w, lb, mean_prob, counts);
   return hipGetLastError();
 }
 

@@ -109,6 +109,12 @@ def test_entry_points_fail_before_any_hip_call():
     assert _lib.lib.moe_route(L, FAKE, 4, FAKE + 4, FAKE, FAKE, FAKE, None, None, FAKE, need, None) == _lib.MOE_ERR_ALIGN
     assert _lib.lib.moe_route(L, FAKE, 4, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, need - 1, None) == _lib.MOE_ERR_WORKSPACE
     assert _lib.lib.moe_route(L, None, 0, None, None, None, None, None, None, None, 0, None) == _lib.MOE_OK
+    assert _lib.lib.moe_load_balance(L, FAKE, 4, None, None, None, FAKE, need, None) == _lib.MOE_ERR_NULL
+    assert _lib.lib.moe_load_balance(L, FAKE + 4, 4, FAKE, None, None, FAKE, need, None) == _lib.MOE_ERR_ALIGN
+    assert _lib.lib.moe_load_balance(L, FAKE, 4, FAKE + 2, None, None, FAKE, need, None) == _lib.MOE_ERR_ALIGN
+    assert _lib.lib.moe_load_balance(L, FAKE, 4, FAKE, FAKE, FAKE, FAKE, need - 1, None) == _lib.MOE_ERR_WORKSPACE
+    assert _lib.lib.moe_load_balance(L, FAKE, -1, FAKE, None, None, FAKE, need, None) == _lib.MOE_ERR_SHAPE
+    assert _lib.lib.moe_load_balance(L, None, 0, None, None, None, None, 0, None) == _lib.MOE_OK
 
 
 def test_python_wrappers_check_inputs():

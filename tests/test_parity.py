@@ -356,3 +356,54 @@ def test_full_forced_routing_one_hot_segment(full):
     assert torch.all(o == o[0:1]).item()
     check_output(xb[:1], bits, d, gi[:1], _np(out.float())[:1], np.arange(1), "forced")
     del moe
+
+
+# ---------------------------------------------------------------------------
+# Load-balance statistic (moe_load_balance).
+# ---------------------------------------------------------------------------
+
+def _check_load_balance(moe, layer, bits, d, xb, tag):
+    x = moe.bits_to_device(xb, "cuda")
+    r = moe.load_balance(x, layer)
+    r2 = moe.load_balance(x, layer)
+    torch.cuda.synchronize()
+    R = O.load_balance(xb, bits, d.K)
+    counts, mp, lb = _np(r["counts"]), _np(r["mean_prob"]).astype(np.float64), float(_np(r["lb"])[0])
+    assert torch.equal(r["lb"], r2["lb"]) and torch.equal(r["mean_prob"], r2["mean_prob"]), f"{tag}: not reproducible"
+    if not R["tie"].any():
+        assert np.array_equal(counts, R["counts"]), f"{tag}: counts differ"
+    else:
+        # Flagged ties may move pairs between tied experts; the total is fixed.
+        assert counts.sum() == R["counts"].sum()
+    # Probabilities from the GPU's fp32 logits, summed in fp32 over the batch.
+    np.testing.assert_allclose(mp, R["mean_prob"], rtol=2e-4, atol=1e-7, err_msg=tag)
+    assert abs(lb - R["lb"]) <= 2e-4 * R["lb"], (tag, lb, R["lb"])
+    _say(f"{tag}: lb {lb:.6f} vs oracle {R['lb']:.6f}, max |dP| {np.abs(mp - R['mean_prob']).max():.2e}")
+    return lb
+
+
+@pytest.mark.parametrize("T", [1, 8, 33, 300, 2049])
+def test_toy_load_balance(toy, T):
+    d, bits, layer = toy
+    moe = _moe()
+    _say(f"case toy load balance T={T}")
+    _check_load_balance(moe, layer, bits, d, mi.make_x(d, T, 3000 + T), f"toy lb T={T}")
+
+
+def test_toy_load_balance_zero_input(toy):
+    d, bits, layer = toy
+    moe = _moe()
+    r = moe.load_balance(torch.zeros((50, d.H), dtype=torch.bfloat16, device="cuda"), layer)
+    torch.cuda.synchronize()
+    assert abs(float(_np(r["lb"])[0]) - 1.0) < 1e-6
+    assert np.array_equal(_np(r["counts"]), np.array([50] * d.K + [0] * (d.E - d.K)))
+
+
+def test_full_load_balance(full):
+    d, bits, layer, zb, zlayer = full
+    moe = _moe()
+    _say("case full load balance decode64 / zipf16384")
+    lb64 = _check_load_balance(moe, layer, bits, d, mi.workload_x(mi.WORKLOADS["decode64"]), "decode64 lb")
+    lbz = _check_load_balance(moe, zlayer, zb, d, mi.workload_x(mi.WORKLOADS["zipf16384"]), "zipf16384 lb")
+    # The skewed workload is far from balanced, the near-uniform one close to it.
+    assert lbz > 2.0 * lb64
