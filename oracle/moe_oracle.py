@@ -36,7 +36,9 @@ notes of this repository):
 * no capacity limit: every (token, expert) pair is computed;
 * the layer output excludes the residual and any norm;
 * the load-balance statistic is E * sum_e f_e * P_e (slot fraction times
-  mean full-softmax probability), the page giving no formula.
+  mean full-softmax probability), the page giving no formula;
+* the MoE sub-block is out = h + MoE(bf16(RMSNorm(h))), RMSNorm the textbook
+  h / sqrt(mean(h^2) + eps) * w.
 
 Inputs are bf16 bit patterns (uint16 arrays); parameters are passed as a
 mapping keyed by the model page's member names: ``gate.weight``,
@@ -298,6 +300,31 @@ def load_balance(x: np.ndarray, params: dict, K: int) -> dict:
     return {"counts": counts.astype(np.int32), "fraction": f, "mean_prob": P,
             "lb": float(E * np.sum(f * P)), "logits": logits, "topk_idx": topk_idx,
             "tie": tie_flags(logits, K)}
+
+
+# ---------------------------------------------------------------------------
+# The MoE sub-block around the layer ("Qwen3.6-35B-A3B — Architecture
+# Overview", Stage 2: Transform Blocks: RMSNorm -> MoE FFN -> +residual; model
+# page, AttentionLayer / DeltaLayer: post_attention_layernorm: RmsNorm<H, T>
+# with param weight [H]).
+# ---------------------------------------------------------------------------
+
+def rmsnorm(h: np.ndarray, norm_w: np.ndarray, eps: float) -> np.ndarray:
+    """y[t] = h[t] / sqrt(mean_j h[t, j]^2 + eps) * w, float64 (bf16 bit inputs).
+
+    The pages give the module and its weight but no formula: the textbook
+    RMSNorm is taken, the weight multiplying directly and eps from the caller.
+    """
+    H = bf16_to_f64(h)
+    w = bf16_to_f64(norm_w).reshape(-1)
+    return H / np.sqrt(np.mean(H * H, axis=1, keepdims=True) + eps) * w[None, :]
+
+
+def block_forward_with_routing(h: np.ndarray, x_bits: np.ndarray, params: dict,
+                               topk_idx: np.ndarray) -> np.ndarray:
+    """h + MoE(x) for given bf16 activations x (the normalised h rounded to
+    bf16, the type the model page gives every activation) and routing."""
+    return bf16_to_f64(h) + forward_with_routing(x_bits, params, topk_idx)
 
 
 def expert_param_count(H: int, I: int) -> int:

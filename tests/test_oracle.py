@@ -449,3 +449,50 @@ def test_load_balance_token_permutation():
     assert np.array_equal(r["counts"], rp["counts"])
     np.testing.assert_allclose(rp["mean_prob"], r["mean_prob"], rtol=1e-12)
     assert abs(rp["lb"] - r["lb"]) < 1e-12 * r["lb"]
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm and the MoE sub-block.
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_closed_forms_and_library():
+    rng = np.random.default_rng(5)
+    H = 64
+    w = _bits(rng.normal(1.0, 0.2, H))
+    wf = O.bf16_to_f64(w)
+    # A constant row c gives sign(c) * w when eps = 0.
+    for c in (0.75, -3.0, 2.0 ** -6):
+        h = _bits(np.full((1, H), c))
+        np.testing.assert_allclose(O.rmsnorm(h, w, 0.0)[0], np.sign(c) * wf, rtol=1e-15, atol=0)
+    h = _bits(rng.normal(0, 1.5, (5, H)))
+    # Unit weight, eps = 0: every output row has mean square exactly one.
+    y = O.rmsnorm(h, _bits(np.ones(H)), 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-14)
+    # Positive scaling of the input leaves it unchanged (eps = 0).
+    h2 = _bits(O.bf16_to_f64(h) * 4.0)
+    np.testing.assert_allclose(O.rmsnorm(h2, w, 0.0), O.rmsnorm(h, w, 0.0), rtol=1e-14)
+    # Brute force with loops and the math module, and torch's rms_norm in float64.
+    eps = 1e-6
+    got = O.rmsnorm(h, w, eps)
+    H64 = O.bf16_to_f64(h)
+    for t in range(H64.shape[0]):
+        ms = sum(v * v for v in H64[t]) / H
+        for j in range(H):
+            assert abs(got[t, j] - H64[t, j] / math.sqrt(ms + eps) * wf[j]) <= 1e-14 * max(1.0, abs(got[t, j]))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(H64), (H,), torch.from_numpy(wf), eps=eps).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_block_forward_reduces_to_residual_and_layer():
+    d = mi.TOY
+    layer = _random_layer(d, 340)
+    h = mi.make_x(d, 7, 341)
+    x = _bits(O.rmsnorm(h, _bits(np.ones(d.H)), 1e-6))
+    idx, _ = O.select_topk(O.router_logits(x, layer["gate.weight"]), d.K)
+    # The sub-block adds the layer's output to the residual stream.
+    np.testing.assert_allclose(O.block_forward_with_routing(h, x, layer, idx) - O.bf16_to_f64(h),
+                               O.forward_with_routing(x, layer, idx), rtol=1e-12, atol=1e-15)
+    # With every down projection zero the sub-block is the identity on h.
+    z = dict(layer, down_proj=np.zeros_like(layer["down_proj"]),
+             **{"shared_expert.down.weight": np.zeros_like(layer["shared_expert.down.weight"])})
+    assert np.array_equal(O.block_forward_with_routing(h, x, z, idx), O.bf16_to_f64(h))
