@@ -243,6 +243,22 @@ def main():
                     "lb": round(float(np.mean([float(r["lb"].item()) for r in lb_out])), 6),
                     "definition": "E * sum_e f_e * P_e (slot fraction x mean full-softmax probability)"}
 
+    # The sub-block form out = h + layer(RMSNorm(h)) on the same batches.
+    norm_w = moe.bits_to_device(
+        mi.f32_to_bf16_bits(np.random.default_rng(11).normal(1.0, 0.2, d.H).astype(np.float32)), "cuda")
+    for i in range(min(warmup, 20)):
+        l = i % nlayers
+        moe.block_forward(xs[l], layers[l], norm_w, 1e-6, out=outs[l], ws=ws)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(lb_steps):
+        l = i % nlayers
+        moe.block_forward(xs[l], layers[l], norm_w, 1e-6, out=outs[l], ws=ws)
+    end.record()
+    torch.cuda.synchronize()
+    block = {"us_per_call": round(start.elapsed_time(end) / lb_steps * 1e3, 2),
+             "definition": "out = h + layer(RMSNorm(h)), eps 1e-6"}
+
     # Kernel attribution: the same steps again, each recording six events at
     # its phase boundaries on the same stream (the fused decode path records
     # its single kernel between events 0 and 1).
@@ -315,6 +331,7 @@ def main():
         "roofline": roof,
         "layer": layer_stats,
         "load_balance": load_balance,
+        "block_forward": block,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

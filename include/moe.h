@@ -130,6 +130,30 @@ int moe_load_balance(const moe_layer_t *L, const void *x, int64_t T, float *lb, 
 int moe_forward(const moe_layer_t *L, const void *x, int64_t T, void *out,
                 void *ws, size_t ws_bytes, void *stream);
 
+/* The MoE sub-block of a transformer block: out = h + MoE(RMSNorm(h))
+ * ("Qwen3.6-35B-A3B — Architecture Overview", Stage 2: Transform Blocks:
+ * RMSNorm -> MoE FFN -> +residual; Linnet model page, AttentionLayer /
+ * DeltaLayer: post_attention_layernorm RmsNorm<H> with weight [H]).
+ *   h       bf16 [T, H]  residual stream entering the sub-block
+ *   norm_w  bf16 [H]     RMSNorm weight; x = bf16(h / sqrt(mean(h^2) + eps) * norm_w)
+ *                        (the textbook RMSNorm: the pages give no formula)
+ *   eps     finite, >= 0
+ *   out     bf16 [T, H]  bf16(h + layer(x)), the residual added to the fp32
+ *                        accumulation before its one rounding
+ * The norm is applied in the fused decode kernel's LDS copy of x (T <= 16) or
+ * by a norm kernel feeding the grouped path; the residual is added where the
+ * output is written (no extra pass over out).  Workspace, alignment, errors
+ * and h/out overlap as moe_forward (h plays the role of x). */
+int moe_block_forward(const moe_layer_t *L, const void *norm_w, float eps, const void *h, int64_t T,
+                      void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* RMSNorm alone (the norm moe_block_forward applies): x = bf16(h[t] /
+ * sqrt(mean_j h[t, j]^2 + eps) * norm_w), fp32 arithmetic, the sum of squares
+ * in a fixed order.  h, x bf16 [T, H], norm_w bf16 [H], 16-byte aligned, H a
+ * positive multiple of 256 (at most 65536), no workspace.  T = 0 is a
+ * successful no-op. */
+int moe_rmsnorm(const void *norm_w, float eps, const void *h, int64_t T, int64_t H, void *x, void *stream);
+
 /* moe_forward that also records caller-created HIP events (hipEvent_t) on
  * `stream` at its phase boundaries, for timing the kernels:
  *   events[0] before the router, [1] after the router (top-K, weights, shared

@@ -159,3 +159,32 @@ def load_balance(x: torch.Tensor, layer: MoeLayer, ws: torch.Tensor | None = Non
     if rc != 0:
         raise MoeError(rc, "moe_load_balance")
     return r
+
+
+def block_forward(h: torch.Tensor, layer: MoeLayer, norm_w: torch.Tensor, eps: float,
+                  out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The MoE sub-block out = h + layer(RMSNorm(h)) (moe_block_forward)."""
+    _check_x(h, layer)
+    if norm_w.dtype != torch.bfloat16 or norm_w.numel() != layer.H or not norm_w.is_contiguous():
+        raise ValueError("norm_w must be a contiguous bf16 tensor of hidden elements")
+    T = h.shape[0]
+    if out is None:
+        out = torch.empty_like(h)
+    if ws is None:
+        ws = layer.workspace(T, h.device)
+    rc = lib.moe_block_forward(layer.desc, _ptr(norm_w), float(eps), _ptr(h), T, _ptr(out), _ptr(ws), ws.numel(),
+                               _stream_handle(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_block_forward")
+    return out
+
+
+def rmsnorm(h: torch.Tensor, norm_w: torch.Tensor, eps: float, stream=None) -> torch.Tensor:
+    """x = bf16(RMSNorm(h)) (moe_rmsnorm); h bf16 [T, H]."""
+    if h.dtype != torch.bfloat16 or h.dim() != 2 or not h.is_contiguous():
+        raise ValueError("h must be a contiguous bf16 [T, H] tensor")
+    x = torch.empty_like(h)
+    rc = lib.moe_rmsnorm(_ptr(norm_w), float(eps), _ptr(h), h.shape[0], h.shape[1], _ptr(x), _stream_handle(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_rmsnorm")
+    return x

@@ -22,7 +22,7 @@ MOE_ERR_LAUNCH = 6
 
 # Exported entry points, as include/moe.h declares them.
 EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_load_balance", "moe_forward",
-           "moe_forward_traced", "moe_strerror", "moe_last_error")
+           "moe_block_forward", "moe_rmsnorm", "moe_forward_traced", "moe_strerror", "moe_last_error")
 
 
 class MoeLayerT(ctypes.Structure):
@@ -65,6 +65,10 @@ def _load():
     lib.moe_load_balance.restype = ctypes.c_int
     lib.moe_forward.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_block_forward.argtypes = [L, P, ctypes.c_float, P, ctypes.c_int64, P, P, ctypes.c_size_t, P]
+    lib.moe_block_forward.restype = ctypes.c_int
+    lib.moe_rmsnorm.argtypes = [P, ctypes.c_float, P, ctypes.c_int64, ctypes.c_int64, P, P]
+    lib.moe_rmsnorm.restype = ctypes.c_int
     lib.moe_forward_traced.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P, P]
     lib.moe_forward_traced.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]

@@ -189,6 +189,7 @@ struct Work {
   bf16_t* h_sh;        // [T, Is]
   bf16_t* y;           // [T*K + T, H]  weighted expert outputs, routed slots then shared rows
   float* psum;         // [nblk * E]  per router block: sum over its tokens of each expert's softmax probability
+  bf16_t* xn;          // [T, H]  RMSNorm of the sub-block input (block form)
 };
 
 }  // namespace moe

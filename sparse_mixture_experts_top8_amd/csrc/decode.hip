@@ -245,6 +245,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();
+    if (a.norm_w) {
+      // Sub-block form: x = bf16(RMSNorm(x)) in place, wave w taking tokens
+      // w, w + 4, ... with the chunk order and wave sum of the standalone
+      // norm kernel (so both give the same bits).
+      const int nch = H / 8;
+      for (int t = wave; t < T; t += kWaves) {
+        bf16_t* xr = s_x + t * kXStride;
+        float ss = 0.f;
+        for (int c = lane; c < nch; c += kWave) {
+          const u32x4 v = ld_lds16(xr + 8 * c);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = bf16_to_f32(v[j] & 0xFFFFu), q = bf16_to_f32(v[j] >> 16);
+            ss += p * p;
+            ss += q * q;
+          }
+        }
+        const float r = 1.0f / sqrtf(wave_sum_f32(ss) / (float)H + a.eps);
+        for (int c = lane; c < nch; c += kWave) {
+          const u32x4 v = ld_lds16(xr + 8 * c), wv = ld16(a.norm_w + 8 * c);
+          u32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j] = pack_bf16x2(bf16_to_f32(v[j] & 0xFFFFu) * r * bf16_to_f32(wv[j] & 0xFFFFu),
+                               bf16_to_f32(v[j] >> 16) * r * bf16_to_f32(wv[j] >> 16));
+          *reinterpret_cast<u32x4*>(xr + 8 * c) = o;
+        }
+      }
+      __syncthreads();
+    }
     if (nrow > 0) {
       const bf16_t* xs = s_x + min(m, T - 1) * kXStride + kbeg + kq;
       const u32x4 z4 = {0u, 0u, 0u, 0u};
@@ -625,7 +655,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const int l = 16 * (i >> 2) + j, c = i & 3;
         return (s_red[0][0][l][c] + s_red[0][1][l][c]) + (s_red[0][2][l][c] + s_red[0][3][l][c]);
       };
-      const float v = split_tok ? (t < 8 ? el(rr, t) : el(8 + rr, t)) : el(rr, t) + el(8 + rr, 8 + t);
+      float v = split_tok ? (t < 8 ? el(rr, t) : el(8 + rr, t)) : el(rr, t) + el(8 + rr, 8 + t);
+      if (a.residual) v = bf16_to_f32(a.residual[(size_t)t * H + row0 + rr]) + v;   // sub-block residual
       a.out[(size_t)t * H + row0 + rr] = (bf16_t)f32_to_bf16(v);
     }
   }

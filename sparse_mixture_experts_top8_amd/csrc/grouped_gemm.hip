@@ -287,7 +287,8 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
 // order, fp32 sum.  The K + 1 row indices and scales are requested first,
 // then all K + 1 rows, so the loads overlap instead of forming a chain.
 constexpr int kMaxK = 8;
-__global__ __launch_bounds__(256) void combine_kernel(int T, int H, int K, Work w, bf16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void combine_kernel(int T, int H, int K, Work w, bf16_t* __restrict__ out,
+                                                      const bf16_t* __restrict__ residual) {
   const int per_tok = H >> 3;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)T * per_tok) return;
@@ -321,6 +322,15 @@ __global__ __launch_bounds__(256) void combine_kernel(int T, int H, int K, Work 
       }
     }
   }
+  if (residual) {
+    // The sub-block's residual add, after the sum: one rounding to bf16.
+    const u32x4 r = ld16(residual + (size_t)t * H + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = bf16_to_f32(r[j] & 0xFFFFu) + acc[2 * j];
+      acc[2 * j + 1] = bf16_to_f32(r[j] >> 16) + acc[2 * j + 1];
+    }
+  }
   u32x4 o;
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
@@ -351,9 +361,11 @@ hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hi
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, bf16_t* out, hipStream_t s) {
+hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, bf16_t* out, hipStream_t s,
+                          const bf16_t* residual) {
   const size_t n = (size_t)T * (L.H / 8);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, L.H, L.K, w, out);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, L.H, L.K, w, out,
+                     residual);
   return hipGetLastError();
 }
 

@@ -46,6 +46,9 @@ struct DecodeArgs {
   int32_t* offsets_out; // route-only: [E + 1]
   int32_t* perm_out;    // route-only: [T*K]
   unsigned long long epoch;   // call-unique; its low 32 bits (never 0) tag this call's logits
+  const bf16_t* norm_w; // optional [H]: x is RMSNorm(x) with this weight (the sub-block form)
+  float eps;            // RMSNorm epsilon
+  const bf16_t* residual;  // optional [T, H]: out = bf16(residual + layer output)
 };
 // Cross-workgroup data of the decode path is published in one copy per XCD
 // (readers poll the copy of their own XCD).
@@ -75,6 +78,10 @@ hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t
 hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
                           int num_cus, hipStream_t s);
 hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s);
-hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, bf16_t* out, hipStream_t s);
+// residual (optional): out = bf16(residual + combined sum), one rounding.
+hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, bf16_t* out, hipStream_t s,
+                          const bf16_t* residual = nullptr);
+// x = bf16(h / sqrt(mean(h^2) + eps) * w), one wave per token.
+hipError_t launch_rmsnorm(const bf16_t* h, const bf16_t* w, float eps, int T, int H, bf16_t* x, hipStream_t s);
 
 }  // namespace moe

@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <cmath>
 #include <unistd.h>
 #include <cstdarg>
 #include <cstdio>
@@ -84,6 +85,7 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   c.w.h_sh = (bf16_t*)take(t * Is * 2);
   c.w.y = (bf16_t*)take((tk + t) * H * 2);
   c.w.psum = (float*)take(nblk * E * 4);
+  c.w.xn = (bf16_t*)take(t * H * 2);
   c.bytes = off;
   return c;
 }
@@ -329,8 +331,11 @@ int moe_load_balance(const moe_layer_t* L, const void* x, int64_t T, float* lb, 
   return launch_status(moe::launch_load_balance(a, t, w, lb, mean_prob, counts, s), "load balance");
 }
 
-int moe_forward_traced(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws,
-                       size_t ws_bytes, void* stream, void* const* events) {
+namespace {
+
+// The layer (norm_w == nullptr) or the sub-block out = x + layer(RMSNorm(x)).
+int forward_impl(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws, size_t ws_bytes,
+                 void* stream, void* const* events, const void* norm_w, float eps) {
   int rc = moe_validate(L, x, T, out, ws, ws_bytes);
   if (rc != MOE_OK || T == 0) return rc;
   int cus = 0, dgrid = 0;
@@ -344,6 +349,11 @@ int moe_forward_traced(const moe_layer_t* L, const void* x, int64_t T, void* out
   if (use_decode(L, T, dgrid)) {
     moe::DecodeArgs da = decode_args(L, x, T, carve_decode(L, T, (char*)ws));
     da.out = (bf16_t*)out;
+    if (norm_w) {
+      da.norm_w = (const bf16_t*)norm_w;
+      da.eps = eps;
+      da.residual = (const bf16_t*)x;
+    }
     if ((rc = launch_status(moe::launch_decode(da, dgrid, s), "decode")) != MOE_OK) return rc;
     for (int i = 1; i <= 5; ++i)
       if ((rc = mark(i)) != MOE_OK) return rc;
@@ -352,21 +362,61 @@ int moe_forward_traced(const moe_layer_t* L, const void* x, int64_t T, void* out
   const moe::Work w = carve(L, T, (char*)ws).w;
   const moe::LayerArgs a = layer_args(L);
   const int t = (int)T;
-  if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, t, w, nullptr, s), "router")) != MOE_OK) return rc;
+  const bf16_t* xin = (const bf16_t*)x;
+  if (norm_w) {
+    if ((rc = launch_status(moe::launch_rmsnorm(xin, (const bf16_t*)norm_w, eps, t, a.H, w.xn, s), "rmsnorm")) !=
+        MOE_OK)
+      return rc;
+    xin = w.xn;
+  }
+  if ((rc = launch_status(moe::launch_router(a, xin, t, w, nullptr, s), "router")) != MOE_OK) return rc;
   if ((rc = mark(1)) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_dispatch(a, t, w, s), "dispatch")) != MOE_OK) return rc;
   if ((rc = mark(2)) != MOE_OK) return rc;
-  if ((rc = launch_status(moe::launch_gate_up(a, (const bf16_t*)x, t, w, cus, s), "gate_up")) != MOE_OK) return rc;
+  if ((rc = launch_status(moe::launch_gate_up(a, xin, t, w, cus, s), "gate_up")) != MOE_OK) return rc;
   if ((rc = mark(3)) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_down(a, t, w, cus, s), "down")) != MOE_OK) return rc;
   if ((rc = mark(4)) != MOE_OK) return rc;
-  if ((rc = launch_status(moe::launch_combine(a, t, w, (bf16_t*)out, s), "combine")) != MOE_OK) return rc;
+  if ((rc = launch_status(moe::launch_combine(a, t, w, (bf16_t*)out, s, norm_w ? (const bf16_t*)x : nullptr),
+                          "combine")) != MOE_OK)
+    return rc;
   return mark(5);
+}
+
+}  // namespace
+
+int moe_forward_traced(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws,
+                       size_t ws_bytes, void* stream, void* const* events) {
+  return forward_impl(L, x, T, out, ws, ws_bytes, stream, events, nullptr, 0.f);
 }
 
 int moe_forward(const moe_layer_t* L, const void* x, int64_t T, void* out, void* ws, size_t ws_bytes,
                 void* stream) {
-  return moe_forward_traced(L, x, T, out, ws, ws_bytes, stream, nullptr);
+  return forward_impl(L, x, T, out, ws, ws_bytes, stream, nullptr, nullptr, 0.f);
+}
+
+int moe_block_forward(const moe_layer_t* L, const void* norm_w, float eps, const void* h, int64_t T, void* out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!norm_w) return fail(MOE_ERR_NULL, "norm_w is NULL");
+  if (!aligned16(norm_w)) return fail(MOE_ERR_ALIGN, "norm_w is not 16-byte aligned");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MOE_ERR_SHAPE, "eps must be finite and >= 0");
+  return forward_impl(L, h, T, out, ws, ws_bytes, stream, nullptr, norm_w, eps);
+}
+
+int moe_rmsnorm(const void* norm_w, float eps, const void* h, int64_t T, int64_t H, void* x, void* stream) {
+  if (T < 0 || T > (int64_t(1) << 22)) return fail(MOE_ERR_SHAPE, "T = %lld out of range", (long long)T);
+  if (H <= 0 || H % 256 || H > (int64_t(1) << 16))
+    return fail(MOE_ERR_SHAPE, "hidden = %lld must be a positive multiple of 256", (long long)H);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MOE_ERR_SHAPE, "eps must be finite and >= 0");
+  if (T == 0) return MOE_OK;
+  if (!norm_w || !h || !x) return fail(MOE_ERR_NULL, "norm_w, h and x are required");
+  if (!aligned16(norm_w) || !aligned16(h) || !aligned16(x)) return fail(MOE_ERR_ALIGN, "a pointer is not 16-byte aligned");
+  int cus = 0, dgrid = 0;
+  int rc = device_check(&cus, &dgrid);
+  if (rc != MOE_OK) return rc;
+  return launch_status(moe::launch_rmsnorm((const bf16_t*)h, (const bf16_t*)norm_w, eps, (int)T, (int)H, (bf16_t*)x,
+                                           (hipStream_t)stream),
+                       "rmsnorm");
 }
 
 const char* moe_strerror(int code) {

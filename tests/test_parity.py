@@ -407,3 +407,84 @@ def test_full_load_balance(full):
     lbz = _check_load_balance(moe, zlayer, zb, d, mi.workload_x(mi.WORKLOADS["zipf16384"]), "zipf16384 lb")
     # The skewed workload is far from balanced, the near-uniform one close to it.
     assert lbz > 2.0 * lb64
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm and the sub-block out = h + layer(RMSNorm(h)).
+# ---------------------------------------------------------------------------
+
+def _bf16_ulp(v):
+    """Spacing of bf16 numbers at |v| (2^(e - 7) for |v| in [2^e, 2^(e+1)))."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def _norm_weight(d, seed):
+    return mi.f32_to_bf16_bits(np.random.default_rng(seed).normal(1.0, 0.2, d.H).astype(np.float32))
+
+
+@pytest.mark.parametrize("T,full_shape", [(37, False), (1000, False), (5, True), (300, True)])
+def test_rmsnorm_parity(T, full_shape):
+    moe = _moe()
+    d = mi.FULL if full_shape else mi.TOY
+    _say(f"case rmsnorm H={d.H} T={T}")
+    hb = mi.make_x(d, T, 7000 + T)
+    wb = _norm_weight(d, 7100 + T)
+    x = moe.rmsnorm(moe.bits_to_device(hb, "cuda"), moe.bits_to_device(wb, "cuda"), 1e-6)
+    torch.cuda.synchronize()
+    got = O.bf16_to_f64(_np(x.view(torch.int16)).view(np.uint16))
+    ref = O.rmsnorm(hb, wb, 1e-6)
+    # Rounded to bf16 from fp32: within one bf16 step of the exact value, and
+    # equal to the correctly rounded value almost everywhere.
+    assert np.all(np.abs(got - ref) <= _bf16_ulp(ref)), f"T={T}"
+    exact = mi.f32_to_bf16_bits(ref.astype(np.float32))
+    frac = np.mean(_np(x.view(torch.int16)).view(np.uint16) != exact)
+    assert frac < 1e-3, frac
+    _say(f"rmsnorm H={d.H} T={T}: elements off by one bf16 step {frac:.2e}")
+
+
+def _check_block(moe, layer, bits, d, hb, wb, tag):
+    h = moe.bits_to_device(hb, "cuda")
+    w = moe.bits_to_device(wb, "cuda")
+    out = moe.block_forward(h, layer, w, 1e-6)
+    x = moe.rmsnorm(h, w, 1e-6)
+    r = moe.route(x, layer)
+    plain = moe.forward(x, layer)
+    torch.cuda.synchronize()
+    xb = _np(x.view(torch.int16)).view(np.uint16)
+    gi = check_routing(xb, bits, d, r, tag)
+    got = _np(out.float()).astype(np.float64)
+    H64 = O.bf16_to_f64(hb)
+    # Against the oracle with the GPU's activations and routing: beyond the
+    # output's own rounding (at the magnitude of h) the layer's tolerance.
+    ref = O.block_forward_with_routing(hb, xb, bits, gi)
+    excess = np.abs(got - ref) - 0.5 * _bf16_ulp(ref)
+    assert excess.max() <= MAX_ABS, (tag, excess.max())
+    # Against the same GPU's layer output plus h: the block rounds once, the
+    # two-step form first rounds the layer output (half a bf16 step at its
+    # magnitude, which can exceed that of the sum when h cancels it) and then
+    # the sum, so they agree within one step of the sum plus half a step of
+    # the layer output.
+    moe_bf16 = _np(plain.float()).astype(np.float64)
+    two_step = H64 + moe_bf16
+    ratio = np.abs(got - two_step) / (_bf16_ulp(two_step) + 0.5 * _bf16_ulp(moe_bf16))
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, (tag, float(ratio.max()), int((ratio > 1).sum()), worst,
+                                float(got[worst]), float(two_step[worst]), float(ref[worst]))
+    _say(f"{tag}: max excess over rounding {excess.max():.3e}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 100])
+def test_toy_block_forward(toy, T):
+    d, bits, layer = toy
+    moe = _moe()
+    _say(f"case toy block T={T}")
+    _check_block(moe, layer, bits, d, mi.make_x(d, T, 7200 + T), _norm_weight(d, 7300 + T), f"toy block T={T}")
+
+
+def test_full_block_forward(full):
+    d, bits, layer, _, _ = full
+    moe = _moe()
+    for T in (1, 16, 64):
+        _say(f"case full block T={T}")
+        _check_block(moe, layer, bits, d, mi.make_x(d, T, 7400 + T), _norm_weight(d, 7500 + T), f"full block T={T}")
