@@ -247,8 +247,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     if (a.norm_w) {
       // Sub-block form: x = bf16(RMSNorm(x)) in place, wave w taking tokens
-      // w, w + 4, ... with the chunk order and wave sum of the standalone
-      // norm kernel (so both give the same bits).
+      // w, w + 4, ... with the expression, chunk order and wave sum of the
+      // standalone norm kernel.
       const int nch = H / 8;
       for (int t = wave; t < T; t += kWaves) {
         bf16_t* xr = s_x + t * kXStride;
