@@ -28,7 +28,13 @@ notes of this repository):
 * rows [0, I) of gate_up_proj[e] are the gate projection, rows [I, 2I) the up
   projection (merged in name order);
 * no biases (none appear in the formulas);
-* router logits are kept in float64, not rounded to bf16;
+* router logits are kept in float64, not rounded to bf16; the second routing
+  mode (``logits_bf16=True``) follows the model page's types instead: the
+  outputs of both gate projections (``gate: Linear<H, Experts, T>`` and
+  ``shared_expert_gate: Linear<H, 1, T>``, T = bf16) are the exact dot
+  products rounded to the nearest bf16 (ties to even), and ranking, softmax
+  and the sigmoid gate all act on those rounded values; equal rounded logits
+  are ordered by expert index like any other tie;
 * rank: higher logit first, equal logits ordered by lower expert index;
   ``topk_idx[t, k]`` lists the selected experts in rank order;
 * SiLU(z) = z * sigmoid(z), sigmoid(z) = 1 / (1 + exp(-z));
@@ -66,6 +72,25 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact decode of bf16 bit patterns: shift into the high half of a float32."""
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value of each float64, ties to the even significand.
+
+    bfloat16 keeps 8 significant bits: in the binade [2^e, 2^(e+1)) its values
+    are spaced 2^(e-7) apart, and below 2^-126 (subnormals) 2^-133 apart.  The
+    value is divided by that spacing, rounded to an integer half-to-even
+    (``np.round``) and scaled back; both steps are exact in float64.
+    Magnitudes that round past the largest finite bf16 become infinite; zeros
+    keep their sign.  Finite inputs assumed.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = 2.0 ** (np.maximum(e, -126.0) - 7.0)
+    r = np.round(v / step) * step
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)
+    return np.where(a == 0, v, r)
 
 
 # ---------------------------------------------------------------------------
@@ -152,18 +177,33 @@ def tie_flags(logits: np.ndarray, K: int, gap: float = TIE_GAP) -> np.ndarray:
     return (gaps < gap).any(axis=1)
 
 
-def route(x: np.ndarray, params: dict, K: int) -> dict:
-    """Router + softmax + top-K + renormalise + shared-expert gate scalar."""
+def route_logits(x: np.ndarray, params: dict, logits_bf16: bool = False) -> np.ndarray:
+    """The router's scores in the chosen mode: float64, or rounded to bf16."""
     logits = router_logits(x, params["gate.weight"])
+    return round_bf16(logits) if logits_bf16 else logits
+
+
+def route(x: np.ndarray, params: dict, K: int, logits_bf16: bool = False) -> dict:
+    """Router + softmax + top-K + renormalise + shared-expert gate scalar.
+
+    With ``logits_bf16`` the scores are rounded to bf16 first; equal scores are
+    then common and are ordered by expert index, so no token is flagged as a
+    tie ("tie" is all False): the choice is fully determined by the rounded
+    scores.
+    """
+    logits = route_logits(x, params, logits_bf16)
     topk_idx, topk_w = select_topk(logits, K)
-    s = shared_gate(x, params)
+    s = shared_gate(x, params, logits_bf16)
+    tie = np.zeros(logits.shape[0], dtype=bool) if logits_bf16 else tie_flags(logits, K)
     return {"logits": logits, "topk_idx": topk_idx, "topk_w": topk_w,
-            "shared_gate": s, "tie": tie_flags(logits, K)}
+            "shared_gate": s, "tie": tie}
 
 
-def shared_gate(x: np.ndarray, params: dict) -> np.ndarray:
-    """s[t] = sigmoid(x[t] . w_sg) for the [1, H] shared_expert_gate Linear."""
-    return sigmoid(bf16_to_f64(x) @ bf16_to_f64(params["shared_expert_gate.weight"]).T)[:, 0]
+def shared_gate(x: np.ndarray, params: dict, logits_bf16: bool = False) -> np.ndarray:
+    """s[t] = sigmoid(x[t] . w_sg) for the [1, H] shared_expert_gate Linear
+    (its output rounded to bf16 first with ``logits_bf16``)."""
+    z = (bf16_to_f64(x) @ bf16_to_f64(params["shared_expert_gate.weight"]).T)[:, 0]
+    return sigmoid(round_bf16(z) if logits_bf16 else z)
 
 
 # ---------------------------------------------------------------------------
@@ -218,11 +258,13 @@ def _dims(params: dict):
 
 
 def forward_with_routing(x: np.ndarray, params: dict, topk_idx: np.ndarray,
-                         topk_w: np.ndarray | None = None) -> np.ndarray:
+                         topk_w: np.ndarray | None = None,
+                         logits_bf16: bool = False) -> np.ndarray:
     """Layer output [T, H] float64 for a given expert choice.
 
     Weights default to the renormalised softmax of the oracle's own logits
-    restricted to ``topk_idx``.  Dispatch goes through ``counting_sort``:
+    (in the routing mode ``logits_bf16`` selects) restricted to ``topk_idx``;
+    the shared-expert gate follows the same mode.  Dispatch goes through ``counting_sort``:
     each expert is evaluated once on the rows routed to it, and each row's
     result is added to its token, scaled by the routing weight.
     """
@@ -230,7 +272,7 @@ def forward_with_routing(x: np.ndarray, params: dict, topk_idx: np.ndarray,
     X = bf16_to_f64(x)
     T, K = np.asarray(topk_idx).shape
     if topk_w is None:
-        topk_w = renormalised_weights(router_logits(x, params["gate.weight"]), topk_idx)
+        topk_w = renormalised_weights(route_logits(x, params, logits_bf16), topk_idx)
     w_flat = np.asarray(topk_w, dtype=np.float64).reshape(-1)
     d = counting_sort(topk_idx, E)
     acc = np.zeros((T, H), dtype=np.float64)
@@ -242,18 +284,18 @@ def forward_with_routing(x: np.ndarray, params: dict, topk_idx: np.ndarray,
         tok = q // K
         Y = routed_expert(X[tok], params, e, I)
         acc[tok] += w_flat[q, None] * Y          # tokens within one segment are distinct
-    s = shared_gate(x, params)
+    s = shared_gate(x, params, logits_bf16)
     return acc + s[:, None] * shared_expert(X, params)
 
 
-def forward(x: np.ndarray, params: dict, K: int) -> np.ndarray:
+def forward(x: np.ndarray, params: dict, K: int, logits_bf16: bool = False) -> np.ndarray:
     """The layer: route, dispatch to the top-K experts, combine, add the gated shared expert."""
-    logits = router_logits(x, params["gate.weight"])
+    logits = route_logits(x, params, logits_bf16)
     topk_idx, topk_w = select_topk(logits, K)
-    return forward_with_routing(x, params, topk_idx, topk_w)
+    return forward_with_routing(x, params, topk_idx, topk_w, logits_bf16)
 
 
-def forward_dense(x: np.ndarray, params: dict, K: int) -> np.ndarray:
+def forward_dense(x: np.ndarray, params: dict, K: int, logits_bf16: bool = False) -> np.ndarray:
     """Brute force for tiny inputs: run all E experts on every token, mask to the top-K.
 
     out[t] = sum_e mask[t, e] * w[t, e] * expert_e(x_t) + s_t * shared(x_t),
@@ -261,7 +303,7 @@ def forward_dense(x: np.ndarray, params: dict, K: int) -> np.ndarray:
     """
     H, E, I = _dims(params)
     X = bf16_to_f64(x)
-    logits = router_logits(x, params["gate.weight"])
+    logits = route_logits(x, params, logits_bf16)
     r = ranks(logits)
     p = softmax_rows(logits)
     mask = (r < K).astype(np.float64)
@@ -270,14 +312,14 @@ def forward_dense(x: np.ndarray, params: dict, K: int) -> np.ndarray:
     out = np.zeros((X.shape[0], H), dtype=np.float64)
     for e in range(E):
         out += w[:, e:e + 1] * routed_expert(X, params, e, I)
-    return out + shared_gate(x, params)[:, None] * shared_expert(X, params)
+    return out + shared_gate(x, params, logits_bf16)[:, None] * shared_expert(X, params)
 
 
 # ---------------------------------------------------------------------------
 # Load-balance statistic (section "MoE FFN: 256 Experts", Load Balancing).
 # ---------------------------------------------------------------------------
 
-def load_balance(x: np.ndarray, params: dict, K: int) -> dict:
+def load_balance(x: np.ndarray, params: dict, K: int, logits_bf16: bool = False) -> dict:
     """Forward-only load-balance statistic of one batch.
 
     The page names an auxiliary loss (coefficient 0.001) that penalises uneven
@@ -291,7 +333,7 @@ def load_balance(x: np.ndarray, params: dict, K: int) -> dict:
     which is 1 when both are uniform and grows as routing concentrates (the
     training loss would be 0.001 * lb; no gradient is formed here).
     """
-    logits = router_logits(x, params["gate.weight"])
+    logits = route_logits(x, params, logits_bf16)
     topk_idx, _ = select_topk(logits, K)
     T, E = logits.shape
     counts = np.bincount(topk_idx.reshape(-1).astype(np.int64), minlength=E)
@@ -299,7 +341,7 @@ def load_balance(x: np.ndarray, params: dict, K: int) -> dict:
     P = softmax_rows(logits).mean(axis=0)
     return {"counts": counts.astype(np.int32), "fraction": f, "mean_prob": P,
             "lb": float(E * np.sum(f * P)), "logits": logits, "topk_idx": topk_idx,
-            "tie": tie_flags(logits, K)}
+            "tie": np.zeros(T, dtype=bool) if logits_bf16 else tie_flags(logits, K)}
 
 
 # ---------------------------------------------------------------------------
@@ -321,10 +363,10 @@ def rmsnorm(h: np.ndarray, norm_w: np.ndarray, eps: float) -> np.ndarray:
 
 
 def block_forward_with_routing(h: np.ndarray, x_bits: np.ndarray, params: dict,
-                               topk_idx: np.ndarray) -> np.ndarray:
+                               topk_idx: np.ndarray, logits_bf16: bool = False) -> np.ndarray:
     """h + MoE(x) for given bf16 activations x (the normalised h rounded to
     bf16, the type the model page gives every activation) and routing."""
-    return bf16_to_f64(h) + forward_with_routing(x_bits, params, topk_idx)
+    return bf16_to_f64(h) + forward_with_routing(x_bits, params, topk_idx, None, logits_bf16)
 
 
 def expert_param_count(H: int, I: int) -> int:

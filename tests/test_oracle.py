@@ -496,3 +496,152 @@ def test_block_forward_reduces_to_residual_and_layer():
     z = dict(layer, down_proj=np.zeros_like(layer["down_proj"]),
              **{"shared_expert.down.weight": np.zeros_like(layer["shared_expert.down.weight"])})
     assert np.array_equal(O.block_forward_with_routing(h, x, z, idx), O.bf16_to_f64(h))
+
+
+# ---------------------------------------------------------------------------
+# bf16-logit routing mode: the model page types the gate projections' outputs
+# as T = bf16.  Rounding pinned against IEEE conversion and exact rationals;
+# routing pinned by a hand-worked case and a loop brute force.
+# ---------------------------------------------------------------------------
+
+def _fraction_round_bf16(v):
+    """Nearest bf16 of a float by exact rational arithmetic (Python's round of a
+    Fraction is half-to-even): v = m 2^e with m in [0.5, 1); bf16 keeps 8 bits
+    of m, so round(m 2^8) 2^(e-8), with the spacing floored at 2^-133."""
+    from fractions import Fraction
+    if v == 0.0:
+        return v
+    _, e = math.frexp(v)
+    shift = max(e - 8, -133)
+    q = round(Fraction(v) / Fraction(2) ** shift)
+    return float(q * Fraction(2) ** shift)
+
+
+def test_round_bf16_matches_ieee_conversion():
+    rng = np.random.default_rng(40)
+    # Random float32 bit patterns over every exponent, subnormals included.
+    bits = rng.integers(0, 0x7F7F0000, size=20000, dtype=np.uint32)
+    bits |= rng.integers(0, 2, size=bits.size, dtype=np.uint32) << np.uint32(31)
+    f = bits.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(f.astype(np.float64)), want)
+    # Midpoints go to the even significand; just above a midpoint goes up,
+    # including offsets that float32 cannot hold (no double rounding).
+    cases = {1 + 2 ** -8: 1.0, 1 + 3 * 2 ** -8: 1 + 2 ** -6, 1 + 2 ** -8 + 2 ** -40: 1 + 2 ** -7,
+             -(1 + 2 ** -8 + 2 ** -40): -(1 + 2 ** -7), 255.5: 256.0, 2.0 ** -140: 0.0,
+             3 * 2.0 ** -134: 2 * 2.0 ** -133,
+             # The largest finite bf16 is (2 - 2^-7) 2^127; above (2 - 2^-8) 2^127 rounds to inf.
+             3.3961e38: (2 - 2 ** -7) * 2.0 ** 127, 3.3963e38: np.inf}
+    got = O.round_bf16(np.array(list(cases)))
+    assert list(got) == list(cases.values())
+    assert math.copysign(1.0, O.round_bf16(np.array([-0.0]))[0]) == -1.0
+
+
+def test_round_bf16_matches_exact_rationals():
+    rng = np.random.default_rng(41)
+    v = rng.standard_normal(3000) * 10.0 ** rng.integers(-40, 38, 3000)
+    np.testing.assert_array_equal(O.round_bf16(v), [_fraction_round_bf16(float(a)) for a in v])
+    # Every bf16 value is a fixed point.
+    b = rng.integers(0, 0x7F80, size=5000).astype(np.uint16)
+    vals = O.bf16_to_f64(b)
+    np.testing.assert_array_equal(O.round_bf16(vals), vals)
+
+
+def _tie_layer():
+    """A toy layer whose router gives expert 7 the score 1 + 2^-9 and expert 2
+    the score 1 (for x = e_0 + 2^-9 e_1): ahead in float64, equal in bf16.
+    Expert 11 scores 1 + 2^-8 (a midpoint: rounds to 1, the even neighbour) and
+    expert 5 scores 1 + 3 * 2^-8 (rounds up to 1 + 2^-6).  The shared-expert
+    gate scores 2^-9 + 2^-18, which rounds to 2^-9."""
+    d = mi.TOY
+    layer = _random_layer(d, 42)
+    r = np.zeros((d.E, d.H), np.float32)
+    r[:, 0] = -1.0
+    r[7, :2] = [1.0, 1.0]
+    r[2, :2] = [1.0, 0.0]
+    r[11, :2] = [1.0, 2.0]
+    r[5, :2] = [1.0, 6.0]
+    layer["gate.weight"] = _bits(r)
+    g = np.zeros((1, d.H), np.float32)
+    g[0, :2] = [2.0 ** -9, 2.0 ** -9]
+    layer["shared_expert_gate.weight"] = _bits(g)
+    x = np.zeros((1, d.H), np.float32)
+    x[0, :2] = [1.0, 2.0 ** -9]
+    return d, layer, _bits(x)
+
+
+def test_route_bf16_hand_worked():
+    d, layer, x = _tie_layer()
+    e9 = 2.0 ** -9
+    f64 = O.route(x, layer, 4)
+    assert list(f64["topk_idx"][0]) == [5, 11, 7, 2]
+    assert f64["logits"][0, 5] == 1 + 6 * e9 and f64["logits"][0, 7] == 1 + e9
+    b = O.route(x, layer, 4, logits_bf16=True)
+    lb = b["logits"][0]
+    assert lb[5] == 1 + 2 ** -6 and lb[11] == 1.0 and lb[7] == 1.0 and lb[2] == 1.0 and lb[0] == -1.0
+    # 11, 7 and 2 tie at 1.0 after rounding: lower index first.
+    assert list(b["topk_idx"][0]) == [5, 2, 7, 11]
+    z = math.exp(2 ** -6)
+    want = np.array([z, 1.0, 1.0, 1.0]) / (z + 3.0)
+    np.testing.assert_allclose(b["topk_w"][0], want, rtol=1e-15)
+    assert not b["tie"].any()
+    # K = 2: the bf16 choice keeps expert 2 where float64 keeps 11.
+    assert list(O.route(x, layer, 2, logits_bf16=True)["topk_idx"][0]) == [5, 2]
+    assert list(O.route(x, layer, 2)["topk_idx"][0]) == [5, 11]
+    assert b["shared_gate"][0] == O.sigmoid(e9)
+    assert f64["shared_gate"][0] == O.sigmoid(e9 + e9 * e9)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_route_bf16_brute_force(seed):
+    rng = np.random.default_rng(43 + seed)
+    T, H, E, K = 5, 16, 10, 3
+    # Coarse values: many scores collide once rounded.
+    x = _bits(rng.integers(-4, 5, (T, H)) * 0.25 + rng.standard_normal((T, H)) * 1e-3)
+    params = {"gate.weight": _bits(rng.integers(-3, 4, (E, H)) * 0.125 + rng.standard_normal((E, H)) * 1e-3),
+              "shared_expert_gate.weight": _bits(rng.standard_normal((1, H)))}
+    # Expert E - 1 copies the router row of expert 1 and expert E - 2 that of
+    # expert 4 with one input's weight moved by less than a bf16 step of the
+    # score: equal in bf16 more often than not.
+    params["gate.weight"][E - 1] = params["gate.weight"][1]
+    params["gate.weight"][E - 2] = params["gate.weight"][4]
+    params["gate.weight"][E - 2, 0] ^= np.uint16(1)
+    R = O.route(x, params, K, logits_bf16=True)
+    xf, wf = O.bf16_to_f64(x), O.bf16_to_f64(params["gate.weight"])
+    gf = O.bf16_to_f64(params["shared_expert_gate.weight"])
+    ties = 0
+    for t in range(T):
+        l = [_fraction_round_bf16(math.fsum(xf[t, h] * wf[e, h] for h in range(H))) for e in range(E)]
+        ties += len(l) - len(set(l))
+        order = sorted(range(E), key=lambda e: (-l[e], e))
+        assert list(R["topk_idx"][t]) == order[:K]
+        assert list(R["logits"][t]) == l
+        ex = [math.exp(l[e] - l[order[0]]) for e in order[:K]]
+        np.testing.assert_allclose(R["topk_w"][t], [v / math.fsum(ex) for v in ex], rtol=1e-14)
+        zg = _fraction_round_bf16(math.fsum(xf[t, h] * gf[0, h] for h in range(H)))
+        assert R["shared_gate"][t] == pytest.approx(1.0 / (1.0 + math.exp(-zg)), rel=1e-15)
+    assert ties > 0
+
+
+def test_route_bf16_scale_and_modes():
+    d = mi.TOY
+    layer = _random_layer(d, 44)
+    x = mi.make_x(d, 40, 45)
+    # Doubling x (exponent + 1, exact for these normal values) doubles every
+    # exact score; rounding to bf16 commutes with it, so the choice and the
+    # rounded scores' ratios are unchanged.
+    x2 = (x + np.uint16(0x80)).astype(np.uint16)
+    assert np.array_equal(O.bf16_to_f64(x2), 2 * O.bf16_to_f64(x))
+    a = O.route(x, layer, d.K, logits_bf16=True)
+    b = O.route(x2, layer, d.K, logits_bf16=True)
+    np.testing.assert_array_equal(b["logits"], 2 * a["logits"])
+    np.testing.assert_array_equal(b["topk_idx"], a["topk_idx"])
+    # The rounded scores differ from float64 by at most half a bf16 step, and
+    # the sparse layer equals the dense brute force in this mode too.
+    f = O.route(x, layer, d.K)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(f["logits"]))) - 7)
+    assert np.all(np.abs(a["logits"] - f["logits"]) <= 0.5 * ulp)
+    np.testing.assert_allclose(O.forward(x, layer, d.K, logits_bf16=True),
+                               O.forward_dense(x, layer, d.K, logits_bf16=True), rtol=1e-12, atol=1e-15)
+    lb = O.load_balance(x, layer, d.K, logits_bf16=True)
+    np.testing.assert_array_equal(lb["topk_idx"], a["topk_idx"])
