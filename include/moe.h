@@ -8,6 +8,7 @@
  * Blocks: SparseMoe, SwiGlu, Linear:
  *
  *   logits[t, e] = x[t] . router_w[e]                              (router)
+ *                  (rounded to bf16 when the layer asks for bf16 scores)
  *   top-K experts per token by logit (ties: lower expert index first),
  *   w[t, k]      = softmax(logits[t])[e_k] / sum_j softmax(logits[t])[e_j]
  *   expert_e(v)  = (SiLU(v Wg_e^T) * (v Wu_e^T)) Wd_e^T,
@@ -77,6 +78,15 @@ typedef struct moe_layer {
   const void *shared_up_w;          /* bf16 [Is, H]     shared_expert.up.weight    */
   const void *shared_down_w;        /* bf16 [H, Is]     shared_expert.down.weight  */
   const void *shared_expert_gate_w; /* bf16 [1, H]      shared_expert_gate.weight  */
+  /* Score precision (Linnet page, Blocks: SparseMoe, whose gate and
+   * shared_expert_gate are Linear<..., T> and whose ranks takes scores of type
+   * T = bf16):
+   *   0  router and shared-gate scores kept in fp32 (accumulation precision);
+   *   1  each score rounded to the nearest bf16 (ties to even) before anything
+   *      uses it: ranking (equal rounded scores order by expert index), the
+   *      softmax weights, the sigmoid gate, and the logits moe_route returns.
+   * Any other value is rejected with MOE_ERR_SHAPE. */
+  int32_t logits_bf16;
 } moe_layer_t;
 
 /* Bytes of device workspace that moe_route / moe_forward need for T tokens
@@ -100,7 +110,8 @@ int moe_validate(const moe_layer_t *L, const void *x, int64_t T, const void *out
  *   perm      int32 [T*K]   pair id q = t*K + k held by each slot, ascending
  *                           t within a segment
  *   shared_gate fp32 [T] or NULL   sigmoid(x[t] . shared_expert_gate_w)
- *   logits    fp32 [T, E] or NULL  router logits (fp32 accumulation)
+ *   logits    fp32 [T, E] or NULL  router logits (fp32 accumulation; the
+ *                                  rounded bf16 values when L->logits_bf16)
  * T = 0 is a successful no-op. */
 int moe_route(const moe_layer_t *L, const void *x, int64_t T,
               int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *perm,
@@ -153,6 +164,19 @@ int moe_block_forward(const moe_layer_t *L, const void *norm_w, float eps, const
  * positive multiple of 256 (at most 65536), no workspace.  T = 0 is a
  * successful no-op. */
 int moe_rmsnorm(const void *norm_w, float eps, const void *h, int64_t T, int64_t H, void *x, void *stream);
+
+/* Rank of every expert in each row of scores (Linnet page, Blocks: SparseMoe,
+ * ranks: integer ranks [R, Experts] of a score tensor [R, Experts]):
+ *   ranks[r, e] = #{j : l[r, j] > l[r, e]} + #{j < e : l[r, j] == l[r, e]}
+ * i.e. 0 for the best score, equal scores ordered by lower expert index, the
+ * same order moe_route selects in (its topk_idx[r, k] is the expert of rank
+ * k).  -0 equals +0; NaN counts as -inf.
+ *   logits  [R, E] device, fp32 (dtype 0, 4-byte aligned) or bf16 (dtype 1,
+ *           2-byte aligned)
+ *   ranks   int32 [R, E] device, 4-byte aligned
+ * 1 <= E <= 256, 0 <= R <= 2^22; R = 0 is a successful no-op.  Asynchronous
+ * on stream; errors as moe_route. */
+int moe_ranks(const void *logits, int32_t dtype, int64_t R, int64_t E, int32_t *ranks, void *stream);
 
 /* moe_forward that also records caller-created HIP events (hipEvent_t) on
  * `stream` at its phase boundaries, for timing the kernels:

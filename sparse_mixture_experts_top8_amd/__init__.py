@@ -50,6 +50,7 @@ class MoeLayer:
     I: int
     Is: int
     params: dict
+    logits_bf16: bool = False   # router / shared-gate scores rounded to bf16
 
     def __post_init__(self):
         p = self.params
@@ -60,13 +61,19 @@ class MoeLayer:
         self.desc = MoeLayerT(self.H, self.E, self.K, self.I, self.Is,
                               _ptr(p["gate.weight"]), _ptr(p["gate_up_proj"]), _ptr(p["down_proj"]),
                               _ptr(p["shared_expert.gate.weight"]), _ptr(p["shared_expert.up.weight"]),
-                              _ptr(p["shared_expert.down.weight"]), _ptr(p["shared_expert_gate.weight"]))
+                              _ptr(p["shared_expert.down.weight"]), _ptr(p["shared_expert_gate.weight"]),
+                              int(self.logits_bf16))
 
     @classmethod
-    def from_bf16_bits(cls, bits: dict, H: int, E: int, K: int, I: int, Is: int, device="cuda"):
+    def from_bf16_bits(cls, bits: dict, H: int, E: int, K: int, I: int, Is: int, device="cuda",
+                       logits_bf16: bool = False):
         """Upload uint16 bf16 bit arrays (numpy) to the device as bfloat16 tensors."""
         p = {n: bits_to_device(bits[n], device) for n in PARAM_NAMES}
-        return cls(H, E, K, I, Is, p)
+        return cls(H, E, K, I, Is, p, logits_bf16)
+
+    def with_logits_bf16(self, on: bool = True) -> "MoeLayer":
+        """The same device parameters with the other score precision."""
+        return MoeLayer(self.H, self.E, self.K, self.I, self.Is, self.params, on)
 
     def workspace_bytes(self, T: int) -> int:
         return int(lib.moe_workspace_bytes(self.desc, int(T)))
@@ -188,3 +195,15 @@ def rmsnorm(h: torch.Tensor, norm_w: torch.Tensor, eps: float, stream=None) -> t
     if rc != 0:
         raise MoeError(rc, "moe_rmsnorm")
     return x
+
+
+def ranks(logits: torch.Tensor, stream=None) -> torch.Tensor:
+    """Stable ranks of every expert per row (moe_ranks); logits fp32 or bf16 [R, E]."""
+    if logits.dim() != 2 or not logits.is_contiguous() or logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be a contiguous fp32 or bf16 [R, E] tensor")
+    out = torch.empty(logits.shape, dtype=torch.int32, device=logits.device)
+    rc = lib.moe_ranks(_ptr(logits), 1 if logits.dtype == torch.bfloat16 else 0, logits.shape[0], logits.shape[1],
+                       _ptr(out), _stream_handle(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_ranks")
+    return out

@@ -22,7 +22,7 @@ MOE_ERR_LAUNCH = 6
 
 # Exported entry points, as include/moe.h declares them.
 EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_load_balance", "moe_forward",
-           "moe_block_forward", "moe_rmsnorm", "moe_forward_traced", "moe_strerror", "moe_last_error")
+           "moe_block_forward", "moe_rmsnorm", "moe_ranks", "moe_forward_traced", "moe_strerror", "moe_last_error")
 
 
 class MoeLayerT(ctypes.Structure):
@@ -39,6 +39,7 @@ class MoeLayerT(ctypes.Structure):
         ("shared_up_w", ctypes.c_void_p),
         ("shared_down_w", ctypes.c_void_p),
         ("shared_expert_gate_w", ctypes.c_void_p),
+        ("logits_bf16", ctypes.c_int32),
     ]
 
 
@@ -69,6 +70,8 @@ def _load():
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_rmsnorm.argtypes = [P, ctypes.c_float, P, ctypes.c_int64, ctypes.c_int64, P, P]
     lib.moe_rmsnorm.restype = ctypes.c_int
+    lib.moe_ranks.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P, P]
+    lib.moe_ranks.restype = ctypes.c_int
     lib.moe_forward_traced.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P, P]
     lib.moe_forward_traced.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]

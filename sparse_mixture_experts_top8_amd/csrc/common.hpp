@@ -26,6 +26,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// The bf16 value nearest to f (ties to even), as a float.
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
@@ -168,6 +171,7 @@ struct LayerArgs {
   const bf16_t* sh_up_w;        // [Is, H]
   const bf16_t* sh_down_w;      // [H, Is]
   const bf16_t* sh_expert_gate; // [H]
+  int logits_bf16;              // 1: router and shared-gate scores rounded to bf16
 };
 
 // Carved workspace (all device pointers).

@@ -295,7 +295,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       if (n < T && mm < nrow) {
         if (mm < n_r) {
           const int e = r_lo + mm;
-          const float v = tile(mm);
+          // Scores typed bf16 (the layer's option) are rounded here, before
+          // anything reads them.
+          const float v = a.L.logits_bf16 ? round_bf16(tile(mm)) : tile(mm);
           if (e < E) {
             // Slot 64 (e % 4) + e / 4 of the token's row: the reader lane that
             // owns experts 4 l .. 4 l + 3 finds them 512 bytes apart, so each
@@ -309,7 +311,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             st_dev(a.gate_s + n, sigmoidf_(v));
           }
         } else if (mm >= p0 && ((mm - p0) & 1) == 0) {
-          const float hv = sigmoidf_(tile(n_r)) * siluf_(tile(mm)) * tile(mm + 1);
+          const float zg = a.L.logits_bf16 ? round_bf16(tile(n_r)) : tile(n_r);
+          const float hv = sigmoidf_(zg) * siluf_(tile(mm)) * tile(mm + 1);
           st_dev(a.h_sh + (size_t)n * Is + s_lo + ((mm - p0) >> 1), (bf16_t)f32_to_bf16(hv));
         }
       }

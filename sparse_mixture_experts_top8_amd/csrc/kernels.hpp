@@ -72,6 +72,8 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
                          float* logits_out, hipStream_t s, float* psum_out = nullptr);
 // Load-balance statistic from the block probability sums and the dispatch
 // offsets: lb [1], mean_prob [E] (optional), counts [E] (optional).
+// Stable ranks of the scores [R, E] (fp32 if dtype == 0, else bf16), E <= 256.
+hipError_t launch_ranks(const void* logits, int dtype, int R, int E, int32_t* ranks, hipStream_t s);
 hipError_t launch_load_balance(const LayerArgs& L, int T, const Work& w, float* lb, float* mean_prob,
                                int32_t* counts, hipStream_t s);
 hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s);

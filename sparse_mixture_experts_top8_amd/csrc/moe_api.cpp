@@ -48,6 +48,8 @@ int check_dims(const moe_layer_t* L, int64_t T) {
   if (K < 1 || K > 8 || K > E) return fail(MOE_ERR_SHAPE, "top_k = %lld must be in [1, min(8, num_experts)]", (long long)K);
   if (I <= 0 || I % 64) return fail(MOE_ERR_SHAPE, "expert_inner = %lld must be a positive multiple of 64", (long long)I);
   if (Is <= 0 || Is % 64) return fail(MOE_ERR_SHAPE, "shared_inner = %lld must be a positive multiple of 64", (long long)Is);
+  if (L->logits_bf16 != 0 && L->logits_bf16 != 1)
+    return fail(MOE_ERR_SHAPE, "logits_bf16 = %d must be 0 or 1", (int)L->logits_bf16);
   return MOE_OK;
 }
 
@@ -168,6 +170,7 @@ moe::LayerArgs layer_args(const moe_layer_t* L) {
   a.sh_up_w = (const bf16_t*)L->shared_up_w;
   a.sh_down_w = (const bf16_t*)L->shared_down_w;
   a.sh_expert_gate = (const bf16_t*)L->shared_expert_gate_w;
+  a.logits_bf16 = L->logits_bf16;
   return a;
 }
 
@@ -417,6 +420,20 @@ int moe_rmsnorm(const void* norm_w, float eps, const void* h, int64_t T, int64_t
   return launch_status(moe::launch_rmsnorm((const bf16_t*)h, (const bf16_t*)norm_w, eps, (int)T, (int)H, (bf16_t*)x,
                                            (hipStream_t)stream),
                        "rmsnorm");
+}
+
+int moe_ranks(const void* logits, int32_t dtype, int64_t R, int64_t E, int32_t* ranks, void* stream) {
+  if (dtype != 0 && dtype != 1) return fail(MOE_ERR_SHAPE, "dtype = %d must be 0 (fp32) or 1 (bf16)", (int)dtype);
+  if (E < 1 || E > 256) return fail(MOE_ERR_SHAPE, "E = %lld must be in [1, 256]", (long long)E);
+  if (R < 0 || R > kMaxTokens) return fail(MOE_ERR_SHAPE, "R = %lld out of range", (long long)R);
+  if (R == 0) return MOE_OK;
+  if (!logits || !ranks) return fail(MOE_ERR_NULL, "logits and ranks are required");
+  if (((uintptr_t)logits & (dtype ? 1u : 3u)) || ((uintptr_t)ranks & 3u))
+    return fail(MOE_ERR_ALIGN, "logits and ranks need their element alignment");
+  int cus = 0, dgrid = 0;
+  int rc = device_check(&cus, &dgrid);
+  if (rc != MOE_OK) return rc;
+  return launch_status(moe::launch_ranks(logits, (int)dtype, (int)R, (int)E, ranks, (hipStream_t)stream), "ranks");
 }
 
 const char* moe_strerror(int code) {

@@ -155,7 +155,15 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs
     // range (reads stay inside the padded row).
 #pragma unroll
     for (int c = 0; c < 4; ++c) lv[j][c] = s_lg[tl][min(4 * lane + c, kMaxRouterCols - 1)];
-    if (tt[j] < T && lane == 0) w.gate_s[tt[j]] = sigmoidf_(s_lg[tl][E]);
+    float zg = s_lg[tl][E];
+    if (L.logits_bf16) {
+      // Scores typed bf16: everything below (ranking, softmax, the gate, the
+      // logits written out) sees the rounded values.
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lv[j][c] = round_bf16(lv[j][c]);
+      zg = round_bf16(zg);
+    }
+    if (tt[j] < T && lane == 0) w.gate_s[tt[j]] = sigmoidf_(zg);
     if (logits_out && tt[j] < T) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -203,6 +211,46 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs
     for (int tl = 0; tl < nt; ++tl) acc += s_lg[tl][tid];
     psum_out[(size_t)blockIdx.x * E + tid] = acc;
   }
+}
+
+// Full stable ranking of each row's scores: rank[e] = the number of experts
+// that score higher, plus those that score the same with a lower index.  One
+// wave per row; the row's order-preserving keys go to LDS, and each lane
+// counts, for its experts e = lane + 64 i, the keys ahead of them (every lane
+// reads the same key at a time, so the reads are broadcasts).
+constexpr int kRankRows = 4;
+
+__global__ __launch_bounds__(64 * kRankRows) void ranks_kernel(const void* __restrict__ logits, int dtype, int R,
+                                                              int E, int32_t* __restrict__ ranks) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_key[kRankRows][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kRankRows + wave;
+  const bool row_ok = r < R;
+  uint32_t mine[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    uint32_t k = 0u;
+    if (row_ok && e < E) {
+      const size_t o = (size_t)r * E + e;
+      const float v = dtype ? bf16_to_f32(static_cast<const bf16_t*>(logits)[o])
+                            : static_cast<const float*>(logits)[o];
+      k = logit_key(v);
+    }
+    if (e < E) s_key[wave][e] = k;
+    mine[i] = k;
+  }
+  __syncthreads();
+  if (!row_ok) return;
+  int cnt[4] = {0, 0, 0, 0};
+  for (int j = 0; j < E; ++j) {
+    const uint32_t kj = s_key[wave][j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt[i] += (kj > mine[i] || (kj == mine[i] && j < lane + 64 * i)) ? 1 : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (lane + 64 * i < E) ranks[(size_t)r * E + lane + 64 * i] = cnt[i];
 }
 
 // Load-balance statistic, one workgroup of 1024 threads: per expert, four
@@ -272,6 +320,12 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(router_select_kernel, dim3(router_blocks(T)), dim3(kSelWaves * 64), 0, s, L, T, ks,
                      (const float*)w.rlog, w, logits_out, psum_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ranks(const void* logits, int dtype, int R, int E, int32_t* ranks, hipStream_t s) {
+  hipLaunchKernelGGL(ranks_kernel, dim3((R + kRankRows - 1) / kRankRows), dim3(64 * kRankRows), 0, s, logits, dtype,
+                     R, E, ranks);
   return hipGetLastError();
 }
 

@@ -128,3 +128,39 @@ def test_python_wrappers_check_inputs():
         moe.forward(torch.zeros(3, 256, dtype=torch.float32), layer)
     with pytest.raises(ValueError):
         moe.MoeLayer(params={n: torch.zeros(4) for n in moe.PARAM_NAMES}, **layer_bits_shape)
+
+
+def test_layer_struct_matches_header(tmp_path):
+    # The ctypes mirror of moe_layer_t has the C compiler's size and offsets.
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "moe.h"\n'
+                   'int main(void) { printf("%zu %zu %zu\\n", sizeof(moe_layer_t), '
+                   'offsetof(moe_layer_t, shared_expert_gate_w), offsetof(moe_layer_t, logits_bf16)); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    size, gate_off, flag_off = map(int, subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.split())
+    assert ctypes.sizeof(_lib.MoeLayerT) == size
+    assert _lib.MoeLayerT.shared_expert_gate_w.offset == gate_off
+    assert _lib.MoeLayerT.logits_bf16.offset == flag_off
+
+
+def test_logits_mode_and_ranks_checks():
+    L = _layer()
+    assert _validate(L) == _lib.MOE_OK
+    L.logits_bf16 = 1
+    assert _validate(L) == _lib.MOE_OK
+    L.logits_bf16 = 2
+    assert _validate(L) == _lib.MOE_ERR_SHAPE and "logits_bf16" in _lib.last_error()
+    assert _lib.lib.moe_workspace_bytes(L, 4) == 0
+    rk = _lib.lib.moe_ranks
+    assert rk(FAKE, 0, 0, 256, FAKE, None) == _lib.MOE_OK
+    assert rk(FAKE, 2, 4, 256, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert rk(FAKE, 0, 4, 0, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert rk(FAKE, 0, 4, 257, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert rk(FAKE, 0, -1, 256, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert rk(None, 0, 4, 256, FAKE, None) == _lib.MOE_ERR_NULL
+    assert rk(FAKE, 0, 4, 256, None, None) == _lib.MOE_ERR_NULL
+    assert rk(FAKE + 2, 0, 4, 256, FAKE, None) == _lib.MOE_ERR_ALIGN
+    assert rk(FAKE, 0, 4, 256, FAKE + 2, None) == _lib.MOE_ERR_ALIGN
+    assert rk(FAKE + 1, 1, 4, 256, FAKE, None) == _lib.MOE_ERR_ALIGN

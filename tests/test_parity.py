@@ -488,3 +488,145 @@ def test_full_block_forward(full):
     for T in (1, 16, 64):
         _say(f"case full block T={T}")
         _check_block(moe, layer, bits, d, mi.make_x(d, T, 7400 + T), _norm_weight(d, 7500 + T), f"full block T={T}")
+
+
+# ---------------------------------------------------------------------------
+# bf16 scores (layer option logits_bf16) and the stable ranks entry point.
+#
+# The GPU rounds its fp32 scores to bf16; the oracle rounds the exact ones.
+# Rounding is monotone, so the GPU's value must lie between the bf16
+# roundings of (exact - bound) and (exact + bound), bound being the fp32
+# error of the dot product; it equals the oracle's unless the exact score lies
+# that close to a rounding midpoint.  Given the GPU's rounded scores, the
+# choice of experts is an exact decision on bf16 values: it must match the
+# oracle's choice from those same values bit for bit, ties included.
+# ---------------------------------------------------------------------------
+
+def _bf16_bracket(exact, bound):
+    return O.round_bf16(exact - bound), O.round_bf16(exact + bound)
+
+
+def check_routing_bf16(xb, bits, dims, r, tag):
+    K, E = dims.K, dims.E
+    T = xb.shape[0]
+    R = O.route(xb, bits, K, logits_bf16=True)
+    exact = O.router_logits(xb, bits["gate.weight"])
+    gi = _np(r["topk_idx"])
+    gl = _np(r["logits"]).astype(np.float64)
+    assert np.array_equal(O.round_bf16(gl), gl), f"{tag}: returned logits are not bf16 values"
+    S = np.abs(O.bf16_to_f64(xb)) @ np.abs(O.bf16_to_f64(bits["gate.weight"])).T
+    lo, hi = _bf16_bracket(exact, LOGIT_CHAIN * 2.0 ** -24 * S)
+    assert np.all((gl >= lo) & (gl <= hi)), f"{tag}: a rounded logit outside its bracket"
+    off = gl != R["logits"]
+    assert np.all(lo[off] != hi[off])
+    # The decision on the GPU's own bf16 scores, bit for bit.
+    want_idx, _ = O.select_topk(gl, K)
+    assert np.array_equal(gi, want_idx), f"{tag}: selection differs from the oracle's on the same scores"
+    same = ~off.any(axis=1)
+    assert np.array_equal(gi[same], R["topk_idx"][same]), tag
+    gw = _np(r["topk_w"]).astype(np.float64)
+    np.testing.assert_allclose(gw, O.renormalised_weights(gl, gi), rtol=0, atol=W_TOL)
+    # Shared gate: the sigmoid of a bf16 value inside the gate score's bracket.
+    zg = (O.bf16_to_f64(xb) @ O.bf16_to_f64(bits["shared_expert_gate.weight"]).T)[:, 0]
+    Sg = np.abs(O.bf16_to_f64(xb)) @ np.abs(O.bf16_to_f64(bits["shared_expert_gate.weight"]))[0]
+    glo, ghi = _bf16_bracket(zg, LOGIT_CHAIN * 2.0 ** -24 * Sg)
+    gs = _np(r["shared_gate"])[:T].astype(np.float64)
+    assert np.all((gs >= O.sigmoid(glo) - W_TOL) & (gs <= O.sigmoid(ghi) + W_TOL)), tag
+    np.testing.assert_allclose(gs[glo == ghi], R["shared_gate"][glo == ghi], rtol=0, atol=W_TOL)
+    d = O.counting_sort(gi, E)
+    assert np.array_equal(_np(r["offsets"]), d["offsets"]), tag
+    assert np.array_equal(_np(r["perm"])[:T * K], d["perm"]), tag
+    # How often rounding made scores equal inside ranks 0..K.
+    srt = np.sort(gl, axis=1)[:, ::-1][:, :K + 1]
+    tied = (np.diff(srt, axis=1) == 0).any(axis=1)
+    _say(f"{tag}: bf16 routing ok, T={T}, tokens with equal scores in ranks 0..K {int(tied.sum())}, "
+         f"scores rounded the other way {int(off.sum())}, tokens whose choice changed with them "
+         f"{int((gi != R['topk_idx']).any(axis=1).sum())}")
+    return gi
+
+
+def check_output_bf16(xb, bits, gi, out_rows, rows, tag):
+    ref = O.forward_with_routing(xb[rows], bits, gi[rows], None, True)
+    got = out_rows.astype(np.float64)
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    _say(f"{tag}: rows {len(rows)} max-abs {err.max():.3e} rel-L2 {rel:.3e}")
+    assert err.max() <= MAX_ABS, tag
+    assert rel <= REL_L2, tag
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 64, 300])
+def test_toy_bf16_logits(toy, T):
+    d, bits, layer = toy
+    lb = layer.with_logits_bf16()
+    _say(f"case toy bf16 logits T={T}")
+    xb = mi.make_x(d, T, 9100 + T)
+    r, out = run_layer(lb, xb, want_logits=True)
+    gi = check_routing_bf16(xb, bits, d, r, f"toy bf16 T={T}")
+    check_output_bf16(xb, bits, gi, _np(out.float()), np.arange(T), f"toy bf16 T={T}")
+    # The fp32 mode on the same layer descriptor's tensors is unaffected.
+    r32, _ = run_layer(layer, xb, want_logits=True)
+    check_routing(xb, bits, d, r32, f"toy fp32 after bf16 T={T}")
+
+
+def test_toy_bf16_zero_input(toy):
+    d, bits, layer = toy
+    for T in (3, 40):
+        r, out = run_layer(layer.with_logits_bf16(), np.zeros((T, d.H), np.uint16), want_logits=True)
+        assert np.all(_np(r["topk_idx"]) == np.arange(d.K))
+        np.testing.assert_allclose(_np(r["topk_w"]), 1.0 / d.K, rtol=0, atol=W_TOL)
+        assert np.all(_np(out.float()) == 0.0)
+
+
+@pytest.mark.parametrize("T", [1, 16, 64, 4096])
+def test_full_bf16_logits(full, T):
+    d, bits, layer, _, _ = full
+    _say(f"case full bf16 logits T={T}")
+    xb = mi.workload_x(mi.WORKLOADS["prefill4096"]) if T == 4096 else mi.make_x(d, T, 9200 + T)
+    r, out = run_layer(layer.with_logits_bf16(), xb, want_logits=True)
+    gi = check_routing_bf16(xb, bits, d, r, f"full bf16 T={T}")
+    rows = np.arange(T) if T <= 64 else _sample_rows(T, gi)
+    check_output_bf16(xb, bits, gi, _np(out.float())[rows], rows, f"full bf16 T={T}")
+
+
+def test_full_bf16_logits_skewed(full):
+    # Scores of size ~50 have a bf16 spacing of 0.25: ties are frequent.
+    d, _, _, zb, zlayer = full
+    wl = mi.WORKLOADS["zipf16384"]
+    xb = mi.workload_x(wl)[:2048]
+    _say("case full bf16 logits, skewed router, T=2048")
+    r, out = run_layer(zlayer.with_logits_bf16(), xb, want_logits=True)
+    gi = check_routing_bf16(xb, zb, d, r, "skewed bf16 T=2048")
+    rows = _sample_rows(2048, gi, int(np.argmax(np.bincount(gi.reshape(-1), minlength=d.E))))
+    check_output_bf16(xb, zb, gi, _np(out.float())[rows], rows, "skewed bf16 T=2048")
+
+
+@pytest.mark.parametrize("E,R", [(1, 3), (7, 5), (16, 1000), (64, 9), (255, 33), (256, 4096)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ranks_parity(E, R, dtype):
+    moe = _moe()
+    rng = np.random.default_rng(E * 7 + R)
+    # Few distinct values: many exact ties; plus signed zeros and infinities.
+    v = (rng.integers(-6, 7, (R, E)) * 0.375).astype(np.float32)
+    v[rng.random((R, E)) < 0.05] = -0.0
+    v[rng.random((R, E)) < 0.02] = np.inf
+    v[rng.random((R, E)) < 0.02] = -np.inf
+    t = torch.from_numpy(v).to("cuda")
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    got = _np(moe.ranks(t))
+    np.testing.assert_array_equal(got, O.ranks(v.astype(np.float64)))
+    assert np.all(np.sort(got, axis=1) == np.arange(E))
+
+
+def test_ranks_agree_with_route(full):
+    moe = _moe()
+    d, bits, layer, _, _ = full
+    xb = mi.make_x(d, 300, 9300)
+    for ly in (layer, layer.with_logits_bf16()):
+        r = moe.route(moe.bits_to_device(xb, "cuda"), ly, want_logits=True)
+        rk = _np(moe.ranks(r["logits"]))
+        gi = _np(r["topk_idx"])
+        np.testing.assert_array_equal(np.take_along_axis(rk, gi.astype(np.int64), axis=1),
+                                      np.broadcast_to(np.arange(d.K), gi.shape))
+        np.testing.assert_array_equal(rk, O.ranks(_np(r["logits"]).astype(np.float64)))
