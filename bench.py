@@ -228,36 +228,45 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / steps
 
+    def time_calls(call, n, warm=0):
+        """Average microseconds of call(i) over n calls back to back on the
+        current stream (events on that stream), after warm untimed calls."""
+        for i in range(warm):
+            call(i)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(n):
+            call(i)
+        end.record()
+        torch.cuda.synchronize()
+        return round(start.elapsed_time(end) / n * 1e3, 2)
+
     # Load-balance statistic of the same batches (moe_load_balance: router,
     # dispatch and the statistic), timed outside the step.
     lb_steps = min(steps, 200)
     lb_out = [moe.load_balance(xs[l], layers[l], ws=ws) for l in range(nlayers)]
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(lb_steps):
-        l = i % nlayers
-        moe.load_balance(xs[l], layers[l], ws=ws)
-    end.record()
-    torch.cuda.synchronize()
-    load_balance = {"us_per_call": round(start.elapsed_time(end) / lb_steps * 1e3, 2),
-                    "lb": round(float(np.mean([float(r["lb"].item()) for r in lb_out])), 6),
-                    "definition": "E * sum_e f_e * P_e (slot fraction x mean full-softmax probability)"}
+    load_balance = {
+        "us_per_call": time_calls(lambda i: moe.load_balance(xs[i % nlayers], layers[i % nlayers], ws=ws), lb_steps),
+        "lb": round(float(np.mean([float(r["lb"].item()) for r in lb_out])), 6),
+        "definition": "E * sum_e f_e * P_e (slot fraction x mean full-softmax probability)"}
 
     # The sub-block form out = h + layer(RMSNorm(h)) on the same batches.
     norm_w = moe.bits_to_device(
         mi.f32_to_bf16_bits(np.random.default_rng(11).normal(1.0, 0.2, d.H).astype(np.float32)), "cuda")
-    for i in range(min(warmup, 20)):
-        l = i % nlayers
-        moe.block_forward(xs[l], layers[l], norm_w, 1e-6, out=outs[l], ws=ws)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(lb_steps):
-        l = i % nlayers
-        moe.block_forward(xs[l], layers[l], norm_w, 1e-6, out=outs[l], ws=ws)
-    end.record()
-    torch.cuda.synchronize()
-    block = {"us_per_call": round(start.elapsed_time(end) / lb_steps * 1e3, 2),
+    block = {"us_per_call": time_calls(lambda i: moe.block_forward(xs[i % nlayers], layers[i % nlayers], norm_w,
+                                                                   1e-6, out=outs[i % nlayers], ws=ws),
+                                       lb_steps, min(warmup, 20)),
              "definition": "out = h + layer(RMSNorm(h)), eps 1e-6"}
+
+    # The layer with bf16 router scores (logits_bf16) on the same batches, and
+    # the stable ranks of one batch's [T, E] scores.
+    layers_b = [ly.with_logits_bf16() for ly in layers]
+    logits_b = moe.route(xs[0], layers_b[0], ws=ws, want_logits=True)["logits"]
+    bf16_logits = {
+        "us_per_call": time_calls(lambda i: moe.forward(xs[i % nlayers], layers_b[i % nlayers],
+                                                        out=outs[i % nlayers], ws=ws), lb_steps, min(warmup, 20)),
+        "ranks_us_per_call": time_calls(lambda i: moe.ranks(logits_b), lb_steps, 5),
+        "definition": "router and shared-gate scores rounded to bf16; ranks of [T, E] fp32 scores"}
 
     # Kernel attribution: the same steps again, each recording six events at
     # its phase boundaries on the same stream (the fused decode path records
@@ -332,6 +341,7 @@ def main():
         "layer": layer_stats,
         "load_balance": load_balance,
         "block_forward": block,
+        "bf16_logits": bf16_logits,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -215,38 +215,43 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs
 
 // Full stable ranking of each row's scores: rank[e] = the number of experts
 // that score higher, plus those that score the same with a lower index.  One
-// wave per row; the row's order-preserving keys go to LDS, and each lane
-// counts, for its experts e = lane + 64 i, the keys ahead of them (every lane
-// reads the same key at a time, so the reads are broadcasts).
+// wave per row.  Each expert gets the 64-bit key (order-preserving score key,
+// then the complement of its index), so "ahead of e" is one unsigned compare;
+// the row's keys go to LDS (padded to a multiple of 2 with key 0, which no
+// score maps to: NaN takes -inf's key), and each lane counts, for its experts
+// e = lane + 64 i, the keys above theirs (every lane reads the same words at
+// a time: broadcasts).  E^2 compares per row: the kernel is ALU-bound.
 constexpr int kRankRows = 4;
 
 __global__ __launch_bounds__(64 * kRankRows) void ranks_kernel(const void* __restrict__ logits, int dtype, int R,
                                                               int E, int32_t* __restrict__ ranks) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_key[kRankRows][256];
+  __shared__ __attribute__((aligned(16))) uint64_t s_key[kRankRows][256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.x * kRankRows + wave;
   const bool row_ok = r < R;
-  uint32_t mine[4];
+  uint64_t mine[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    uint32_t k = 0u;
+    uint64_t k = 0u;
     if (row_ok && e < E) {
       const size_t o = (size_t)r * E + e;
       const float v = dtype ? bf16_to_f32(static_cast<const bf16_t*>(logits)[o])
                             : static_cast<const float*>(logits)[o];
-      k = logit_key(v);
+      k = ((uint64_t)logit_key(v) << 32) | (uint32_t)(0xFFFFu - e);
     }
-    if (e < E) s_key[wave][e] = k;
+    s_key[wave][e] = k;   // e < 256: the whole padded row is written
     mine[i] = k;
   }
   __syncthreads();
   if (!row_ok) return;
   int cnt[4] = {0, 0, 0, 0};
-  for (int j = 0; j < E; ++j) {
-    const uint32_t kj = s_key[wave][j];
+  const int E2 = (E + 1) & ~1;
+#pragma unroll 4
+  for (int j0 = 0; j0 < E2; j0 += 2) {
+    const uint64_t k0 = s_key[wave][j0], k1 = s_key[wave][j0 + 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cnt[i] += (kj > mine[i] || (kj == mine[i] && j < lane + 64 * i)) ? 1 : 0;
+    for (int i = 0; i < 4; ++i) cnt[i] += (int)(k0 > mine[i]) + (int)(k1 > mine[i]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
