@@ -59,7 +59,8 @@ enum moe_status {
   MOE_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned             */
   MOE_ERR_WORKSPACE = 4, /* ws_bytes < moe_workspace_bytes(L, T)                */
   MOE_ERR_DEVICE = 5,    /* the current HIP device is not a gfx950              */
-  MOE_ERR_LAUNCH = 6     /* a HIP call failed; moe_last_error() has its text    */
+  MOE_ERR_LAUNCH = 6,    /* a HIP call failed; moe_last_error() has its text    */
+  MOE_ERR_MEMORY = 7     /* memory of the wrong kind or too small an allocation */
 };
 
 /* One MoE layer: dimensions and device pointers to its seven parameters
@@ -177,6 +178,38 @@ int moe_rmsnorm(const void *norm_w, float eps, const void *h, int64_t T, int64_t
  * 1 <= E <= 256, 0 <= R <= 2^22; R = 0 is a successful no-op.  Asynchronous
  * on stream; errors as moe_route. */
 int moe_ranks(const void *logits, int32_t dtype, int64_t R, int64_t E, int32_t *ranks, void *stream);
+
+/* Device bytes of an expert cache with `capacity` slots for moe_forward_streamed:
+ * each slot holds one routed expert's gate_up [2I, H] and down [H, I] bf16
+ * weights (6 MiB at H = 2048, I = 512).  0 if capacity < 1 or the dimensions
+ * are unsupported.  Host-only; no HIP call. */
+size_t moe_expert_cache_bytes(const moe_layer_t *L, int32_t capacity);
+
+/* The layer with its routed experts' weights in host memory, streamed into a
+ * device cache on demand ("One Token Through Qwen3.6" (InferedThoughts),
+ * Where the Weights Live: weights pass from system RAM into GPU memory, the
+ * hierarchy made explicit; One Complete Decode Step: routing decides which
+ * expert weights a layer needs).
+ *   L->gate_up_w, L->down_w  pinned host memory (hipHostMalloc), [E, 2I, H]
+ *                            and [E, H, I] bf16, 16-byte aligned; every other
+ *                            weight in device memory as for moe_forward
+ *   cache, cache_bytes       device memory, 16-byte aligned; its slot count
+ *                            C = min(E, cache_bytes / moe_expert_cache_bytes(L, 1))
+ *                            must be at least 1
+ * The router and dispatch run on the device as in moe_forward; then the
+ * touched experts (ascending index) are processed in rounds of C: each round
+ * copies its experts' weights from host memory into the cache (a device
+ * kernel reading the host mapping: no host synchronisation, the whole call
+ * stays asynchronous on `stream`) and runs the grouped GEMMs on them.  Only
+ * touched experts cross the host link (U * 6 MiB for U touched experts).
+ * Results equal moe_forward's grouped path for the same inputs bit for bit
+ * (T > 16; smaller batches use the grouped path here, not the fused decode
+ * kernel).  The cache holds no state between calls; calls sharing a cache
+ * must be ordered on one stream.  MOE_ERR_MEMORY if gate_up_w or down_w is not
+ * pinned host memory or its allocation is smaller than E experts.  Other
+ * arguments, workspace and errors as moe_forward. */
+int moe_forward_streamed(const moe_layer_t *L, const void *x, int64_t T, void *out, void *cache,
+                         size_t cache_bytes, void *ws, size_t ws_bytes, void *stream);
 
 /* moe_forward that also records caller-created HIP events (hipEvent_t) on
  * `stream` at its phase boundaries, for timing the kernels:

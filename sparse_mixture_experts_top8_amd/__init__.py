@@ -207,3 +207,28 @@ def ranks(logits: torch.Tensor, stream=None) -> torch.Tensor:
     if rc != 0:
         raise MoeError(rc, "moe_ranks")
     return out
+
+
+def expert_cache(layer: MoeLayer, capacity: int, device="cuda") -> torch.Tensor:
+    """Device memory for an expert cache of ``capacity`` slots (moe_expert_cache_bytes)."""
+    n = int(lib.moe_expert_cache_bytes(layer.desc, int(capacity)))
+    if n == 0:
+        raise ValueError("capacity must be at least 1")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def forward_streamed(x: torch.Tensor, layer: MoeLayer, cache: torch.Tensor, out: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The layer with gate_up_proj / down_proj in pinned host memory, the routed
+    experts streamed into ``cache`` on demand (moe_forward_streamed)."""
+    _check_x(x, layer)
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if ws is None:
+        ws = layer.workspace(T, x.device)
+    rc = lib.moe_forward_streamed(layer.desc, _ptr(x), T, _ptr(out), _ptr(cache), cache.numel(), _ptr(ws),
+                                  ws.numel(), _stream_handle(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_forward_streamed")
+    return out

@@ -19,10 +19,12 @@ MOE_ERR_ALIGN = 3
 MOE_ERR_WORKSPACE = 4
 MOE_ERR_DEVICE = 5
 MOE_ERR_LAUNCH = 6
+MOE_ERR_MEMORY = 7
 
 # Exported entry points, as include/moe.h declares them.
 EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_load_balance", "moe_forward",
-           "moe_block_forward", "moe_rmsnorm", "moe_ranks", "moe_forward_traced", "moe_strerror", "moe_last_error")
+           "moe_block_forward", "moe_rmsnorm", "moe_ranks", "moe_expert_cache_bytes", "moe_forward_streamed",
+           "moe_forward_traced", "moe_strerror", "moe_last_error")
 
 
 class MoeLayerT(ctypes.Structure):
@@ -70,6 +72,10 @@ def _load():
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_rmsnorm.argtypes = [P, ctypes.c_float, P, ctypes.c_int64, ctypes.c_int64, P, P]
     lib.moe_rmsnorm.restype = ctypes.c_int
+    lib.moe_expert_cache_bytes.argtypes = [L, ctypes.c_int32]
+    lib.moe_expert_cache_bytes.restype = ctypes.c_size_t
+    lib.moe_forward_streamed.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P, ctypes.c_size_t, P]
+    lib.moe_forward_streamed.restype = ctypes.c_int
     lib.moe_ranks.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P, P]
     lib.moe_ranks.restype = ctypes.c_int
     lib.moe_forward_traced.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P, P]

@@ -103,22 +103,37 @@ template <bool GATE_UP>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
                                                              Work w, const int* __restrict__ prefix,
                                                              const int4* __restrict__ tdesc,
-                                                             const int* __restrict__ slot_tok) {
+                                                             const int* __restrict__ slot_tok,
+                                                             const int* __restrict__ window,
+                                                             const int* __restrict__ slot_map) {
   __shared__ __attribute__((aligned(1024))) char lds[NS * kATile];
 
   const int E = L.E, K = L.K, H = L.H;
   // Tile of this workgroup: XCD x = blockIdx % 8 takes the x-th contiguous
-  // eighth of the tile list, in order.
-  const int ntiles = uni(prefix[E + 1]);
+  // eighth of the tile list, in order.  With a window (streamed experts) the
+  // list is two ranges of the dispatch list: {first, count} of one round's
+  // routed tiles, then {first, count} of shared tiles.
+  int ntiles, lo0 = 0, n0, lo1 = 0;
+  if (window) {
+    lo0 = uni(window[0]);
+    n0 = uni(window[1]);
+    lo1 = uni(window[2]);
+    ntiles = n0 + uni(window[3]);
+  } else {
+    ntiles = uni(prefix[E + 1]);
+    n0 = ntiles;
+  }
   const int chunk = (ntiles + 7) >> 3;
   const int j8 = blockIdx.x >> 3;
   if (j8 >= chunk) return;
   const int t = (blockIdx.x & 7) * chunk + j8;
   if (t >= ntiles) return;
-  const int4 d = tdesc[t];
+  const int4 d = tdesc[t < n0 ? lo0 + t : lo1 + (t - n0)];
   const int g = uni(d.x), seg0 = uni(d.y), nrows = uni(d.z);
   const int m0 = uni(d.w & 0xFFFF) * BM, nt = uni(d.w >> 16);
   const bool shared = g == E;
+  // Weight block of the group: its expert index, or its cache slot.
+  const int gw = (slot_map && !shared) ? uni(slot_map[g]) : g;
   const int kdim = GATE_UP ? H : (shared ? L.Is : L.I);
   const int inner_n = shared ? L.Is : L.I;           // gate_up: inner rows of the group
   const int nreal = kdim / BK;                       // real k-steps
@@ -160,12 +175,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
       b_rs[1] = make_rsrc(L.sh_up_w, (uint32_t)(L.Is * H * 2));
       b_off[0] = b_off[1] = 2u * (uint32_t)(inner * H + 16 * q);
     } else {
-      b_rs[0] = b_rs[1] = make_rsrc(L.gate_up_w + (size_t)g * 2 * L.I * H, (uint32_t)(2 * L.I * H * 2));
+      b_rs[0] = b_rs[1] = make_rsrc(L.gate_up_w + (size_t)gw * 2 * L.I * H, (uint32_t)(2 * L.I * H * 2));
       b_off[0] = 2u * (uint32_t)(inner * H + 16 * q);
       b_off[1] = 2u * (uint32_t)((L.I + inner) * H + 16 * q);
     }
   } else {
-    const bf16_t* base = shared ? L.sh_down_w : L.down_w + (size_t)g * H * L.I;
+    const bf16_t* base = shared ? L.sh_down_w : L.down_w + (size_t)gw * H * L.I;
     b_rs[0] = b_rs[1] = make_rsrc(base, (uint32_t)(H * kdim * 2));
 #pragma unroll
     for (int b = 0; b < 2; ++b) b_off[b] = 2u * (uint32_t)((nt * BN + 32 * wv + 16 * b + l16) * kdim + 16 * q);
@@ -342,22 +357,23 @@ unsigned gemm_grid(int64_t bound) { return (unsigned)(8 * ((bound + 7) / 8)); }
 }  // namespace
 
 hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work& w, int num_cus,
-                          hipStream_t s) {
+                          hipStream_t s, const int* window, const int* slot_map) {
   (void)num_cus;
   // The dispatch tables go in as separate read-only arguments: uniform reads of
   // them then compile to scalar loads.
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, 2 * L.I, 2 * L.Is);
   hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(gemm_grid(bound)), dim3(256), 0, s, L, x, T, w,
-                     (const int*)w.tiles_gu, (const int4*)w.tdesc_gu, (const int*)w.slot_tok);
+                     (const int*)w.tiles_gu, (const int4*)w.tdesc_gu, (const int*)w.slot_tok, window, slot_map);
   return hipGetLastError();
 }
 
-hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s) {
+hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s, const int* window,
+                       const int* slot_map) {
   (void)num_cus;
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, L.H, L.H);
   hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(gemm_grid(bound)), dim3(256), 0, s, L,
                      (const bf16_t*)nullptr, T, w, (const int*)w.tiles_dn, (const int4*)w.tdesc_dn,
-                     (const int*)w.slot_tok);
+                     (const int*)w.slot_tok, window, slot_map);
   return hipGetLastError();
 }
 

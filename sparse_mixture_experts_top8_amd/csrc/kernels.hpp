@@ -77,9 +77,18 @@ hipError_t launch_ranks(const void* logits, int dtype, int R, int E, int32_t* ra
 hipError_t launch_load_balance(const LayerArgs& L, int T, const Work& w, float* lb, float* mean_prob,
                                int32_t* counts, hipStream_t s);
 hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s);
+// window (optional): int4 {first routed tile, count, first shared tile, count}
+// selecting part of the dispatch tile list; slot_map (optional): expert ->
+// weight block index (cache slot) for the routed groups.
 hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
-                          int num_cus, hipStream_t s);
-hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s);
+                          int num_cus, hipStream_t s, const int* window = nullptr, const int* slot_map = nullptr);
+hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s,
+                       const int* window = nullptr, const int* slot_map = nullptr);
+// Streamed experts: plan the rounds after dispatch (C slots, R rounds), then
+// per round copy its experts from host memory into the slots.
+hipError_t launch_stream_plan(const LayerArgs& L, const Work& w, int C, int R, hipStream_t s);
+hipError_t launch_stream_copy(const LayerArgs& L, const void* host_gu, const void* host_dn, void* slot_gu,
+                              void* slot_dn, const Work& w, int C, int r, hipStream_t s);
 // residual (optional): out = bf16(residual + combined sum), one rounding.
 hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, bf16_t* out, hipStream_t s,
                           const bf16_t* residual = nullptr);

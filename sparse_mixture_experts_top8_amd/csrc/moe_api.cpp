@@ -88,6 +88,10 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   c.w.y = (bf16_t*)take((tk + t) * H * 2);
   c.w.psum = (float*)take(nblk * E * 4);
   c.w.xn = (bf16_t*)take(t * H * 2);
+  c.w.st_list = (int32_t*)take((E + 1) * 4);
+  c.w.st_slot = (int32_t*)take(E * 4);
+  c.w.st_win_gu = (int32_t*)take(E * 16);
+  c.w.st_win_dn = (int32_t*)take(E * 16);
   c.bytes = off;
   return c;
 }
@@ -436,6 +440,92 @@ int moe_ranks(const void* logits, int32_t dtype, int64_t R, int64_t E, int32_t* 
   return launch_status(moe::launch_ranks(logits, (int)dtype, (int)R, (int)E, ranks, (hipStream_t)stream), "ranks");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Bytes of one expert's gate_up and down weights.
+size_t expert_gu_bytes(const moe_layer_t* L) { return (size_t)2 * L->expert_inner * L->hidden * 2; }
+size_t expert_dn_bytes(const moe_layer_t* L) { return (size_t)L->hidden * L->expert_inner * 2; }
+
+// p must lie in pinned host memory whose allocation holds [p, p + need);
+// *dev receives the device address of p.
+int host_span(const void* p, size_t need, const char* name, const void** dev) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess || at.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_MEMORY, "%s is not pinned host memory (allocate it with hipHostMalloc)", name);
+  }
+  void* base = nullptr;
+  size_t size = 0;
+  if (hipPointerGetAttribute(&base, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, (hipDeviceptr_t)p) != hipSuccess ||
+      hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, (hipDeviceptr_t)p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_MEMORY, "%s: the extent of its allocation cannot be queried", name);
+  }
+  const size_t at_off = (size_t)((const char*)p - (const char*)base);
+  if ((const char*)p < (const char*)base || at_off > size || size - at_off < need)
+    return fail(MOE_ERR_MEMORY, "%s: its allocation holds %zu bytes from it, %zu needed", name,
+                at_off <= size ? size - at_off : (size_t)0, need);
+  void* dbase = nullptr;
+  if (hipHostGetDevicePointer(&dbase, base, 0) != hipSuccess || !dbase) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_MEMORY, "%s: no device mapping for its host allocation", name);
+  }
+  *dev = (const char*)dbase + at_off;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_expert_cache_bytes(const moe_layer_t* L, int32_t capacity) {
+  if (check_dims(L, 1) != MOE_OK || capacity < 1) return 0;
+  return (size_t)capacity * (expert_gu_bytes(L) + expert_dn_bytes(L));
+}
+
+int moe_forward_streamed(const moe_layer_t* L, const void* x, int64_t T, void* out, void* cache,
+                         size_t cache_bytes, void* ws, size_t ws_bytes, void* stream) {
+  int rc = moe_validate(L, x, T, out, ws, ws_bytes);
+  if (rc != MOE_OK || T == 0) return rc;
+  if (!cache) return fail(MOE_ERR_NULL, "the expert cache is NULL");
+  if (!aligned16(cache)) return fail(MOE_ERR_ALIGN, "the expert cache is not 16-byte aligned");
+  const size_t gu = expert_gu_bytes(L), dn = expert_dn_bytes(L);
+  const int64_t E = L->num_experts;
+  const int64_t C = std::min<int64_t>((int64_t)(cache_bytes / (gu + dn)), E);
+  if (C < 1) return fail(MOE_ERR_WORKSPACE, "the expert cache has %zu bytes, one slot needs %zu", cache_bytes, gu + dn);
+  int cus = 0, dgrid = 0;
+  if ((rc = device_check(&cus, &dgrid)) != MOE_OK) return rc;
+  const void *host_gu = nullptr, *host_dn = nullptr;
+  if ((rc = host_span(L->gate_up_w, (size_t)E * gu, "gate_up_w", &host_gu)) != MOE_OK) return rc;
+  if ((rc = host_span(L->down_w, (size_t)E * dn, "down_w", &host_dn)) != MOE_OK) return rc;
+  const int64_t R = (std::min<int64_t>(E, T * L->top_k) + C - 1) / C;
+  const moe::Work w = carve(L, T, (char*)ws).w;
+  moe::LayerArgs a = layer_args(L);
+  char* slot_gu = (char*)cache;
+  char* slot_dn = slot_gu + (size_t)C * gu;
+  hipStream_t s = (hipStream_t)stream;
+  const int t = (int)T;
+  if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, t, w, nullptr, s), "router")) != MOE_OK) return rc;
+  if ((rc = launch_status(moe::launch_dispatch(a, t, w, s), "dispatch")) != MOE_OK) return rc;
+  if ((rc = launch_status(moe::launch_stream_plan(a, w, (int)C, (int)R, s), "stream plan")) != MOE_OK) return rc;
+  // The GEMMs read routed weights from the slots, indexed by slot.
+  a.gate_up_w = (const bf16_t*)slot_gu;
+  a.down_w = (const bf16_t*)slot_dn;
+  for (int64_t r = 0; r < R; ++r) {
+    if ((rc = launch_status(moe::launch_stream_copy(a, host_gu, host_dn, slot_gu, slot_dn, w, (int)C, (int)r, s),
+                            "stream copy")) != MOE_OK)
+      return rc;
+    if ((rc = launch_status(moe::launch_gate_up(a, (const bf16_t*)x, t, w, cus, s, w.st_win_gu + 4 * r, w.st_slot),
+                            "gate_up")) != MOE_OK)
+      return rc;
+    if ((rc = launch_status(moe::launch_down(a, t, w, cus, s, w.st_win_dn + 4 * r, w.st_slot), "down")) != MOE_OK)
+      return rc;
+  }
+  return launch_status(moe::launch_combine(a, t, w, (bf16_t*)out, s), "combine");
+}
+
 const char* moe_strerror(int code) {
   switch (code) {
     case MOE_OK: return "ok";
@@ -445,6 +535,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_DEVICE: return "current device is not a gfx950";
     case MOE_ERR_LAUNCH: return "a HIP call failed";
+    case MOE_ERR_MEMORY: return "memory of the wrong kind or extent";
     default: return "unknown status code";
   }
 }

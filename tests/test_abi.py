@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_codes():
-    for code in range(7):
+    for code in range(8):
         assert _lib.strerror(code) and _lib.strerror(code) != "unknown status code"
     assert _lib.strerror(99) == "unknown status code"
 
@@ -164,3 +164,20 @@ def test_logits_mode_and_ranks_checks():
     assert rk(FAKE + 2, 0, 4, 256, FAKE, None) == _lib.MOE_ERR_ALIGN
     assert rk(FAKE, 0, 4, 256, FAKE + 2, None) == _lib.MOE_ERR_ALIGN
     assert rk(FAKE + 1, 1, 4, 256, FAKE, None) == _lib.MOE_ERR_ALIGN
+
+
+def test_streamed_entry_point_checks():
+    L = _layer()
+    per = _lib.lib.moe_expert_cache_bytes(L, 1)
+    assert per == (2 * 512 * 2048 + 2048 * 512) * 2
+    assert _lib.lib.moe_expert_cache_bytes(L, 8) == 8 * per
+    assert _lib.lib.moe_expert_cache_bytes(L, 0) == 0
+    assert _lib.lib.moe_expert_cache_bytes(_layer(H=100), 4) == 0
+    need = _lib.lib.moe_workspace_bytes(L, 4)
+    fs = _lib.lib.moe_forward_streamed
+    assert fs(L, None, 0, None, None, 0, None, 0, None) == _lib.MOE_OK
+    assert fs(L, FAKE, 4, FAKE, None, per, FAKE, need, None) == _lib.MOE_ERR_NULL
+    assert fs(L, FAKE, 4, FAKE, FAKE + 8, per, FAKE, need, None) == _lib.MOE_ERR_ALIGN
+    assert fs(L, FAKE, 4, FAKE, FAKE, per - 1, FAKE, need, None) == _lib.MOE_ERR_WORKSPACE
+    assert fs(L, FAKE, 4, FAKE, FAKE, per, FAKE, need - 1, None) == _lib.MOE_ERR_WORKSPACE
+    assert fs(L, FAKE, -2, FAKE, FAKE, per, FAKE, need, None) == _lib.MOE_ERR_SHAPE

@@ -630,3 +630,102 @@ def test_ranks_agree_with_route(full):
         np.testing.assert_array_equal(np.take_along_axis(rk, gi.astype(np.int64), axis=1),
                                       np.broadcast_to(np.arange(d.K), gi.shape))
         np.testing.assert_array_equal(rk, O.ranks(_np(r["logits"]).astype(np.float64)))
+
+
+# ---------------------------------------------------------------------------
+# Routed experts streamed from pinned host memory (moe_forward_streamed).
+# The GEMMs are the same kernels reading the same values from cache slots, so
+# against moe_forward's grouped path (T > 16) the output is bit for bit the
+# same, whatever the number of rounds; at every T it is checked against the
+# oracle too.
+# ---------------------------------------------------------------------------
+
+def _host_layer(layer):
+    moe = _moe()
+    p = dict(layer.params)
+    p["gate_up_proj"] = p["gate_up_proj"].cpu().pin_memory()
+    p["down_proj"] = p["down_proj"].cpu().pin_memory()
+    return moe.MoeLayer(layer.H, layer.E, layer.K, layer.I, layer.Is, p, layer.logits_bf16)
+
+
+@pytest.fixture(scope="module")
+def toy_host(toy):
+    d, bits, layer = toy
+    return _host_layer(layer)
+
+
+@pytest.mark.parametrize("T", [1, 5, 17, 64, 300])
+@pytest.mark.parametrize("cap", [16, 3, 1])
+def test_toy_streamed(toy, toy_host, T, cap):
+    moe = _moe()
+    d, bits, layer = toy
+    _say(f"case toy streamed T={T} slots={cap}")
+    xb = mi.make_x(d, T, 9400 + T)
+    x = moe.bits_to_device(xb, "cuda")
+    cache = moe.expert_cache(toy_host, cap)
+    got = moe.forward_streamed(x, toy_host, cache)
+    ref = moe.forward(x, layer)
+    r = moe.route(x, layer, want_logits=True)
+    torch.cuda.synchronize()
+    gi = check_routing(xb, bits, d, r, f"toy streamed T={T}")
+    check_output(xb, bits, d, gi, _np(got.float()), np.arange(T), f"toy streamed T={T} slots={cap}")
+    if T > 16:
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), "streamed != resident"
+
+
+def test_toy_streamed_cache_reuse(toy, toy_host):
+    # A cache that served other batches (and more rounds) gives the same bits.
+    moe = _moe()
+    d, bits, layer = toy
+    xa = moe.bits_to_device(mi.make_x(d, 300, 9500), "cuda")
+    xb = moe.bits_to_device(mi.make_x(d, 40, 9501), "cuda")
+    fresh = moe.forward_streamed(xb, toy_host, moe.expert_cache(toy_host, 2))
+    cache = moe.expert_cache(toy_host, 2)
+    for _ in range(2):
+        moe.forward_streamed(xa, toy_host, cache)
+        again = moe.forward_streamed(xb, toy_host, cache)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), fresh.view(torch.int16))
+    assert torch.equal(again.view(torch.int16), moe.forward(xb, layer).view(torch.int16))
+
+
+def test_streamed_rejects_wrong_memory(toy, toy_host):
+    moe = _moe()
+    d, bits, layer = toy
+    x = moe.bits_to_device(mi.make_x(d, 20, 9600), "cuda")
+    cache = moe.expert_cache(toy_host, 4)
+    # Experts in device memory, in pageable host memory, or in a pinned
+    # allocation holding half of them (torch's pinned allocator rounds sizes
+    # up to a power of two, so a buffer only slightly short would be padded
+    # to the full size): refused before anything is launched.
+    p = dict(toy_host.params)
+    bad = {"device": dict(p, gate_up_proj=layer.params["gate_up_proj"]),
+           "pageable": dict(p, down_proj=p["down_proj"].clone()),
+           "short": dict(p, down_proj=torch.empty((d.E // 2) * d.H * d.I, dtype=torch.bfloat16).pin_memory())}
+    for name, params in bad.items():
+        try:
+            moe.forward_streamed(x, moe.MoeLayer(d.H, d.E, d.K, d.I, d.Is, params), cache)
+        except moe.MoeError as e:
+            assert e.code == moe._lib.MOE_ERR_MEMORY, (name, str(e))
+            _say(f"{name}: {e}")
+        else:
+            pytest.fail(f"{name}: not refused")
+
+
+@pytest.mark.parametrize("T,cap", [(1, 8), (16, 256), (64, 40), (4096, 256)])
+def test_full_streamed(full, T, cap):
+    moe = _moe()
+    d, bits, layer, _, _ = full
+    host = _host_layer(layer)
+    _say(f"case full streamed T={T} slots={cap}")
+    xb = mi.workload_x(mi.WORKLOADS["prefill4096"]) if T == 4096 else mi.make_x(d, T, 9700 + T)
+    x = moe.bits_to_device(xb, "cuda")
+    got = moe.forward_streamed(x, host, moe.expert_cache(host, cap))
+    ref = moe.forward(x, layer)
+    r = moe.route(x, layer, want_logits=True)
+    torch.cuda.synchronize()
+    gi = check_routing(xb, bits, d, r, f"full streamed T={T}")
+    rows = np.arange(T) if T <= 64 else _sample_rows(T, gi)
+    check_output(xb, bits, d, gi, _np(got.float())[rows], rows, f"full streamed T={T} slots={cap}")
+    if T > 16:
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), "streamed != resident"
