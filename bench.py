@@ -268,6 +268,26 @@ def main():
         "ranks_us_per_call": time_calls(lambda i: moe.ranks(logits_b), lb_steps, 5),
         "definition": "router and shared-gate scores rounded to bf16; ranks of [T, E] fp32 scores"}
 
+    # Routed experts streamed from pinned host memory (moe_forward_streamed)
+    # into a device cache big enough for one round; the bytes that cross the
+    # host link per call are the touched experts' weights.
+    host_params = dict(layers[0].params)
+    host_params["gate_up_proj"] = host_params["gate_up_proj"].cpu().pin_memory()
+    host_params["down_proj"] = host_params["down_proj"].cpu().pin_memory()
+    host_layer = moe.MoeLayer(d.H, d.E, d.K, d.I, d.Is, host_params)
+    cache = moe.expert_cache(host_layer, min(d.E, T * d.K))
+    U_host = [int((torch.bincount(moe.route(x, layers[0], ws=ws)["topk_idx"].view(-1).long(),
+                                  minlength=d.E) > 0).sum()) for x in xs]
+    st_calls = 20 if T <= 16 else 4
+    st_us = time_calls(lambda i: moe.forward_streamed(xs[i % nlayers], host_layer, cache, out=outs[i % nlayers],
+                                                      ws=ws), st_calls, 2)
+    st_bytes = float(np.mean([U_host[i % nlayers] for i in range(st_calls)])) * 3 * d.H * d.I * 2
+    streamed = {"us_per_call": st_us, "slots": min(d.E, T * d.K),
+                "host_bytes_per_call": int(st_bytes),
+                "host_link_GBps": round(st_bytes / (st_us * 1e-6) / 1e9, 2),
+                "definition": "routed experts' weights in pinned host memory, touched ones copied per call"}
+    del host_params, host_layer, cache
+
     # Kernel attribution: the same steps again, each recording six events at
     # its phase boundaries on the same stream (the fused decode path records
     # its single kernel between events 0 and 1).
@@ -342,6 +362,7 @@ def main():
         "load_balance": load_balance,
         "block_forward": block,
         "bf16_logits": bf16_logits,
+        "streamed": streamed,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
