@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--workload", default="decode1", choices=sorted(DEFAULTS))
     ap.add_argument("--layers", type=int, default=None, help="weight sets rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row-major", action="store_true",
+                    help="keep the routed experts row-major instead of the MFMA-tile layout")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -198,6 +200,10 @@ def main():
     t0 = time.time()
     base_bits = mi.workload_layer(wl)
     layers = [device_layer(moe, mi, wl, l, base_bits) for l in range(nlayers)]
+    if not args.row_major:
+        # Load-time layout: the routed experts rewritten once into the
+        # MFMA-tile layout (moe_tile_experts; same values, same results).
+        layers = [ly.tiled() for ly in layers]
     xs = [device_x(moe, mi, wl, l) for l in range(nlayers)]
     outs = [torch.empty_like(x) for x in xs]
     ws = layers[0].workspace(T)
@@ -274,7 +280,7 @@ def main():
     host_params = dict(layers[0].params)
     host_params["gate_up_proj"] = host_params["gate_up_proj"].cpu().pin_memory()
     host_params["down_proj"] = host_params["down_proj"].cpu().pin_memory()
-    host_layer = moe.MoeLayer(d.H, d.E, d.K, d.I, d.Is, host_params)
+    host_layer = moe.MoeLayer(d.H, d.E, d.K, d.I, d.Is, host_params, False, layers[0].experts_tiled)
     cache = moe.expert_cache(host_layer, min(d.E, T * d.K))
     U_host = [int((torch.bincount(moe.route(x, layers[0], ws=ws)["topk_idx"].view(-1).long(),
                                   minlength=d.E) > 0).sum()) for x in xs]
@@ -356,6 +362,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.note}; H={d.H} E={d.E} K={d.K} I={d.I} Is={d.Is} T={T}",
                    "tokens_per_step": T, "layers_rotated": nlayers, "weights": "seeded N(0,0.02) bf16",
+                   "expert_layout": "row-major" if args.row_major else "mfma-tile",
                    "device": prop.name, "cus": prop.multi_processor_count},
         "roofline": roof,
         "layer": layer_stats,

@@ -88,6 +88,10 @@ typedef struct moe_layer {
    *      softmax weights, the sigmoid gate, and the logits moe_route returns.
    * Any other value is rejected with MOE_ERR_SHAPE. */
   int32_t logits_bf16;
+  /* Layout of gate_up_w and down_w: 0 row-major as above; 1 the MFMA-tile
+   * layout moe_tile_experts writes (same values in other places; every path
+   * gives the same bits with either layout). */
+  int32_t experts_tiled;
 } moe_layer_t;
 
 /* Bytes of device workspace that moe_route / moe_forward need for T tokens
@@ -178,6 +182,19 @@ int moe_rmsnorm(const void *norm_w, float eps, const void *h, int64_t T, int64_t
  * 1 <= E <= 256, 0 <= R <= 2^22; R = 0 is a successful no-op.  Asynchronous
  * on stream; errors as moe_route. */
 int moe_ranks(const void *logits, int32_t dtype, int64_t R, int64_t E, int32_t *ranks, void *stream);
+
+/* Rewrite the routed experts' weights of L (row-major, device memory) into
+ * the MFMA-tile layout: for each expert, each block of 16 consecutive rows and
+ * each 64-wide k-step, 2 KB ordered half h (0, 1), lane l (0..63), 8 elements,
+ * lane l holding row 16 * block + l % 16 and k-step elements
+ * 16 (l / 16) + 8 h .. + 7.  Each load instruction of the grouped GEMMs then
+ * reads 1 KB of consecutive bytes.
+ *   gate_up_tiled  device, E * 2I * H bf16, 16-byte aligned, not overlapping
+ *   down_tiled     device, E * H * I bf16, 16-byte aligned, not overlapping
+ * A layer descriptor with these pointers and experts_tiled = 1 gives results
+ * bit-identical to the row-major layer's grouped path.  Asynchronous on
+ * stream; errors as moe_forward (MOE_ERR_SHAPE if L is already tiled). */
+int moe_tile_experts(const moe_layer_t *L, void *gate_up_tiled, void *down_tiled, void *stream);
 
 /* Device bytes of an expert cache with `capacity` slots for moe_forward_streamed:
  * each slot holds one routed expert's gate_up [2I, H] and down [H, I] bf16

@@ -51,6 +51,7 @@ class MoeLayer:
     Is: int
     params: dict
     logits_bf16: bool = False   # router / shared-gate scores rounded to bf16
+    experts_tiled: bool = False  # gate_up_proj / down_proj in the MFMA-tile layout
 
     def __post_init__(self):
         p = self.params
@@ -62,7 +63,7 @@ class MoeLayer:
                               _ptr(p["gate.weight"]), _ptr(p["gate_up_proj"]), _ptr(p["down_proj"]),
                               _ptr(p["shared_expert.gate.weight"]), _ptr(p["shared_expert.up.weight"]),
                               _ptr(p["shared_expert.down.weight"]), _ptr(p["shared_expert_gate.weight"]),
-                              int(self.logits_bf16))
+                              int(self.logits_bf16), int(self.experts_tiled))
 
     @classmethod
     def from_bf16_bits(cls, bits: dict, H: int, E: int, K: int, I: int, Is: int, device="cuda",
@@ -73,7 +74,18 @@ class MoeLayer:
 
     def with_logits_bf16(self, on: bool = True) -> "MoeLayer":
         """The same device parameters with the other score precision."""
-        return MoeLayer(self.H, self.E, self.K, self.I, self.Is, self.params, on)
+        return MoeLayer(self.H, self.E, self.K, self.I, self.Is, self.params, on, self.experts_tiled)
+
+    def tiled(self, stream=None) -> "MoeLayer":
+        """A copy of the layer with its routed experts in the MFMA-tile layout
+        (moe_tile_experts); the other parameters are shared."""
+        p = dict(self.params)
+        p["gate_up_proj"] = torch.empty_like(p["gate_up_proj"])
+        p["down_proj"] = torch.empty_like(p["down_proj"])
+        rc = lib.moe_tile_experts(self.desc, _ptr(p["gate_up_proj"]), _ptr(p["down_proj"]), _stream_handle(stream))
+        if rc != 0:
+            raise MoeError(rc, "moe_tile_experts")
+        return MoeLayer(self.H, self.E, self.K, self.I, self.Is, p, self.logits_bf16, True)
 
     def workspace_bytes(self, T: int) -> int:
         return int(lib.moe_workspace_bytes(self.desc, int(T)))

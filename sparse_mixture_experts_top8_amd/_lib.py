@@ -23,7 +23,7 @@ MOE_ERR_MEMORY = 7
 
 # Exported entry points, as include/moe.h declares them.
 EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_load_balance", "moe_forward",
-           "moe_block_forward", "moe_rmsnorm", "moe_ranks", "moe_expert_cache_bytes", "moe_forward_streamed",
+           "moe_block_forward", "moe_rmsnorm", "moe_ranks", "moe_tile_experts", "moe_expert_cache_bytes", "moe_forward_streamed",
            "moe_forward_traced", "moe_strerror", "moe_last_error")
 
 
@@ -42,6 +42,7 @@ class MoeLayerT(ctypes.Structure):
         ("shared_down_w", ctypes.c_void_p),
         ("shared_expert_gate_w", ctypes.c_void_p),
         ("logits_bf16", ctypes.c_int32),
+        ("experts_tiled", ctypes.c_int32),
     ]
 
 
@@ -72,6 +73,8 @@ def _load():
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_rmsnorm.argtypes = [P, ctypes.c_float, P, ctypes.c_int64, ctypes.c_int64, P, P]
     lib.moe_rmsnorm.restype = ctypes.c_int
+    lib.moe_tile_experts.argtypes = [L, P, P, P]
+    lib.moe_tile_experts.restype = ctypes.c_int
     lib.moe_expert_cache_bytes.argtypes = [L, ctypes.c_int32]
     lib.moe_expert_cache_bytes.restype = ctypes.c_size_t
     lib.moe_forward_streamed.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P, ctypes.c_size_t, P]

@@ -172,6 +172,7 @@ struct LayerArgs {
   const bf16_t* sh_down_w;      // [H, Is]
   const bf16_t* sh_expert_gate; // [H]
   int logits_bf16;              // 1: router and shared-gate scores rounded to bf16
+  int tiled;                    // 1: routed expert weights in the MFMA-tile layout
 };
 
 // Carved workspace (all device pointers).

@@ -466,14 +466,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // Down-projection weights of stage s for this lane's row (zeros from
   // outside the resource for stages past the last, empty halves, rows past
   // nrows and k-steps past the inner size).
+  // MFMA step ks (32 wide) is half ks & 1 of the 64-wide step ks >> 1, lane
+  // quarter q holding its elements 16 q + 8 (ks & 1) .. + 7: in row-major
+  // weights 16 bytes of the row, in the tile layout 16 bytes of the 1 KB that
+  // half occupies.
   auto issue_a = [&](u32x4 (&st)[kMaxISteps], int s) {
-    uint32_t off = kOutside;
+    uint32_t off = kOutside, ks2 = 128u, ks1 = 16u;
     if (row_ok && s < NS) {
       if (s == 0) {
-        if (split_tok || hm == 0) off = 2u * (uint32_t)(crow * Is + kq);
+        if (split_tok || hm == 0) off = 2u * (uint32_t)(crow * Is + 2 * kq);
       } else {
         const int e = stage_expert(s, hm);
-        if (e >= 0) off = 2u * (uint32_t)((e * H + crow) * I + kq);
+        if (e >= 0) {
+          if (L.tiled) {
+            off = 2u * (uint32_t)(e * H * I) + 2048u * (uint32_t)((crow >> 4) * (I / 64)) +
+                  16u * (uint32_t)(2 * kq + (crow & 15));
+            ks2 = 2048u;
+            ks1 = 1024u;
+          } else {
+            off = 2u * (uint32_t)((e * H + crow) * I + 2 * kq);
+          }
+        }
       }
     }
     const rsrc_t rs = s == 0 ? r_sdn : r_dn;
@@ -481,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s4 = 0; s4 < kMaxISteps; ++s4) {
       const int ks = kMaxISteps * wave + s4;
-      st[s4] = ldw_buf(rs, ks < nk ? off + 64u * ks : kOutside);
+      st[s4] = ldw_buf(rs, ks < nk ? off + ks2 * (uint32_t)(ks >> 1) + ks1 * (uint32_t)(ks & 1) : kOutside);
     }
   };
 
@@ -498,26 +511,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const rsrc_t r_gu = make_rsrc(L.gate_up_w, (size_t)E * 2 * I * H * 2);
     // Stage loads are issued unconditionally: past the last block, and for
     // k-steps past H / 4, the offsets fall outside the resource.
+    // MFMA step ks is half ks & 1 of this wave's 64-wide step ks >> 1 (lane
+    // quarter q: elements 16 q + 8 (ks & 1) .. + 7), for row-major and tiled
+    // weights alike.
+    const uint32_t ks2 = L.tiled ? 2048u : 128u, ks1 = L.tiled ? 1024u : 16u;
     auto issue = [&](u32x4 (&st)[kMaxHSteps], int i) {
       uint32_t off = kOutside;
       if (i < nmine) {
         const int b = wg + i * G, u = b / nbi, i0 = 8 * (b - u * nbi);
         const int e = s_touched[u];
-        const int row = e * 2 * I + ((m & 2) ? I : 0) + i0 + 2 * (m >> 2) + (m & 1);
-        off = 2u * (uint32_t)(row * H + kbeg + kq);
+        const int r = ((m & 2) ? I : 0) + i0 + 2 * (m >> 2) + (m & 1);   // row of the expert's [2I, H]
+        if (L.tiled)
+          off = 2u * (uint32_t)(e * 2 * I * H) + 2048u * (uint32_t)((r >> 4) * (H / 64) + kbeg / 64) +
+                16u * (uint32_t)(2 * kq + (r & 15));
+        else
+          off = 2u * (uint32_t)((e * 2 * I + r) * H + kbeg + 2 * kq);
       }
 #pragma unroll
-      for (int ks = 0; ks < kMaxHSteps; ++ks) st[ks] = ldw_buf(r_gu, ks < nks ? off + 64u * ks : kOutside);
+      for (int ks = 0; ks < kMaxHSteps; ++ks)
+        st[ks] = ldw_buf(r_gu, ks < nks ? off + ks2 * (uint32_t)(ks >> 1) + ks1 * (uint32_t)(ks & 1) : kOutside);
     };
     auto compute = [&](u32x4 (&st)[kMaxHSteps], int i) {
       if (i < nmine) {
         const int b = wg + i * G, u = b / nbi, i0 = 8 * (b - u * nbi);
         const int e = s_touched[u], beg = s_off[e], cnt = s_off[e + 1] - beg;
         const int t = s_list[beg + min(m, cnt - 1)] / K;
-        const bf16_t* xs = s_x + t * kXStride + kbeg + kq;
+        const bf16_t* xs = s_x + t * kXStride + kbeg + 2 * kq;
         u32x4 xb[kMaxHSteps];
 #pragma unroll
-        for (int ks = 0; ks < kMaxHSteps; ++ks) xb[ks] = ld_lds16(xs + 32 * min(ks, nks - 1));
+        for (int ks = 0; ks < kMaxHSteps; ++ks) {
+          const int kc = min(ks, nks - 1);
+          xb[ks] = ld_lds16(xs + 64 * (kc >> 1) + 8 * (kc & 1));
+        }
         f32x4 d = zf4;
 #pragma unroll
         for (int ks = 0; ks < kMaxHSteps; ++ks) d = mfma16(st[ks], xb[ks], d);
@@ -618,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s4 = 0; s4 < kMaxISteps; ++s4) {
         const int ks = kMaxISteps * wave + s4;
-        st[s4] = ld_after16(rs, ks < nk ? row + 2u * (uint32_t)(32 * ks + kq) : kOutside);
+        st[s4] = ld_after16(rs, ks < nk ? row + 2u * (uint32_t)(64 * (ks >> 1) + 8 * (ks & 1) + 2 * kq) : kOutside);
       }
     };
     // Two accumulators (even and odd k-steps) halve the MFMA dependency chain.

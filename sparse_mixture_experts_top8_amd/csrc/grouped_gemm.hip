@@ -168,7 +168,23 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
   // each k-step (two 16-byte loads), through a buffer resource.
   rsrc_t b_rs[2];
   uint32_t b_off[2];
-  if (GATE_UP) {
+  // Byte steps between k-steps and between the two halves of a k-step: row
+  // major, or the MFMA-tile layout of routed experts (16-row block, k-step,
+  // half, lane: one contiguous 1 KB per load instruction).
+  const bool tiled = L.tiled && !shared;
+  const uint32_t k_stride = tiled ? 2048u : 2u * BK, h_stride = tiled ? 1024u : 16u;
+  if (tiled) {
+    const int nk = kdim / BK;
+    if (GATE_UP) {
+      b_rs[0] = b_rs[1] = make_rsrc(L.gate_up_w + (size_t)gw * 2 * L.I * H, (uint32_t)(2 * L.I * H * 2));
+      b_off[0] = 2048u * (uint32_t)((nt * 4 + wv) * nk) + 16u * lane;
+      b_off[1] = 2048u * (uint32_t)((L.I / 16 + nt * 4 + wv) * nk) + 16u * lane;
+    } else {
+      b_rs[0] = b_rs[1] = make_rsrc(L.down_w + (size_t)gw * H * L.I, (uint32_t)(H * kdim * 2));
+#pragma unroll
+      for (int b = 0; b < 2; ++b) b_off[b] = 2048u * (uint32_t)((nt * 8 + 2 * wv + b) * nk) + 16u * lane;
+    }
+  } else if (GATE_UP) {
     const int inner = min(nt * 64 + 16 * wv + l16, inner_n - 1);   // past the inner size: repeated, dropped
     if (shared) {
       b_rs[0] = make_rsrc(L.sh_gate_w, (uint32_t)(L.Is * H * 2));
@@ -200,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         wbs[b][h] = __builtin_amdgcn_raw_buffer_load_b128(
-            b_rs[b], real ? b_off[b] + 2u * (uint32_t)(ks * BK + 8 * h) : kOutside, 0, 0);
+            b_rs[b], real ? b_off[b] + k_stride * (uint32_t)ks + h_stride * h : kOutside, 0, 0);
   };
 
   f32x4 acc[kMBlocks][2];

@@ -84,6 +84,8 @@ hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work
                           int num_cus, hipStream_t s, const int* window = nullptr, const int* slot_map = nullptr);
 hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s,
                        const int* window = nullptr, const int* slot_map = nullptr);
+// [E, R, Kd] row-major bf16 -> the MFMA-tile layout (R % 16 == 0, Kd % 64 == 0).
+hipError_t launch_pack_tiles(const bf16_t* src, bf16_t* dst, int E, int R, int Kd, hipStream_t s);
 // Streamed experts: plan the rounds after dispatch (C slots, R rounds), then
 // per round copy its experts from host memory into the slots.
 hipError_t launch_stream_plan(const LayerArgs& L, const Work& w, int C, int R, hipStream_t s);

@@ -50,6 +50,8 @@ int check_dims(const moe_layer_t* L, int64_t T) {
   if (Is <= 0 || Is % 64) return fail(MOE_ERR_SHAPE, "shared_inner = %lld must be a positive multiple of 64", (long long)Is);
   if (L->logits_bf16 != 0 && L->logits_bf16 != 1)
     return fail(MOE_ERR_SHAPE, "logits_bf16 = %d must be 0 or 1", (int)L->logits_bf16);
+  if (L->experts_tiled != 0 && L->experts_tiled != 1)
+    return fail(MOE_ERR_SHAPE, "experts_tiled = %d must be 0 or 1", (int)L->experts_tiled);
   return MOE_OK;
 }
 
@@ -175,6 +177,7 @@ moe::LayerArgs layer_args(const moe_layer_t* L) {
   a.sh_down_w = (const bf16_t*)L->shared_down_w;
   a.sh_expert_gate = (const bf16_t*)L->shared_expert_gate_w;
   a.logits_bf16 = L->logits_bf16;
+  a.tiled = L->experts_tiled;
   return a;
 }
 
@@ -479,6 +482,24 @@ int host_span(const void* p, size_t need, const char* name, const void** dev) {
 }  // namespace
 
 extern "C" {
+
+int moe_tile_experts(const moe_layer_t* L, void* gate_up_tiled, void* down_tiled, void* stream) {
+  int rc = check_dims(L, 1);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_weights(L)) != MOE_OK) return rc;
+  if (L->experts_tiled) return fail(MOE_ERR_SHAPE, "the layer's experts are already tiled");
+  if (!gate_up_tiled || !down_tiled) return fail(MOE_ERR_NULL, "gate_up_tiled and down_tiled are required");
+  if (!aligned16(gate_up_tiled) || !aligned16(down_tiled)) return fail(MOE_ERR_ALIGN, "an output is not 16-byte aligned");
+  int cus = 0, dgrid = 0;
+  if ((rc = device_check(&cus, &dgrid)) != MOE_OK) return rc;
+  const int E = L->num_experts, H = L->hidden, I = L->expert_inner;
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = launch_status(moe::launch_pack_tiles((const bf16_t*)L->gate_up_w, (bf16_t*)gate_up_tiled, E, 2 * I, H, s),
+                          "tile gate_up")) != MOE_OK)
+    return rc;
+  return launch_status(moe::launch_pack_tiles((const bf16_t*)L->down_w, (bf16_t*)down_tiled, E, H, I, s),
+                       "tile down");
+}
 
 size_t moe_expert_cache_bytes(const moe_layer_t* L, int32_t capacity) {
   if (check_dims(L, 1) != MOE_OK || capacity < 1) return 0;
