@@ -134,15 +134,17 @@ def test_layer_struct_matches_header(tmp_path):
     # The ctypes mirror of moe_layer_t has the C compiler's size and offsets.
     src = tmp_path / "layout.c"
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "moe.h"\n'
-                   'int main(void) { printf("%zu %zu %zu\\n", sizeof(moe_layer_t), '
-                   'offsetof(moe_layer_t, shared_expert_gate_w), offsetof(moe_layer_t, logits_bf16)); return 0; }\n')
+                   'int main(void) { printf("%zu %zu %zu %zu\\n", sizeof(moe_layer_t), '
+                   'offsetof(moe_layer_t, shared_expert_gate_w), offsetof(moe_layer_t, logits_bf16), '
+                   'offsetof(moe_layer_t, experts_tiled)); return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
-    size, gate_off, flag_off = map(int, subprocess.run([str(exe)], capture_output=True, text=True,
-                                                       check=True).stdout.split())
+    size, gate_off, flag_off, tiled_off = map(int, subprocess.run([str(exe)], capture_output=True, text=True,
+                                                                  check=True).stdout.split())
     assert ctypes.sizeof(_lib.MoeLayerT) == size
     assert _lib.MoeLayerT.shared_expert_gate_w.offset == gate_off
     assert _lib.MoeLayerT.logits_bf16.offset == flag_off
+    assert _lib.MoeLayerT.experts_tiled.offset == tiled_off
 
 
 def test_logits_mode_and_ranks_checks():
@@ -181,3 +183,16 @@ def test_streamed_entry_point_checks():
     assert fs(L, FAKE, 4, FAKE, FAKE, per - 1, FAKE, need, None) == _lib.MOE_ERR_WORKSPACE
     assert fs(L, FAKE, 4, FAKE, FAKE, per, FAKE, need - 1, None) == _lib.MOE_ERR_WORKSPACE
     assert fs(L, FAKE, -2, FAKE, FAKE, per, FAKE, need, None) == _lib.MOE_ERR_SHAPE
+
+
+def test_tile_experts_checks():
+    L = _layer()
+    te = _lib.lib.moe_tile_experts
+    assert te(L, None, FAKE, None) == _lib.MOE_ERR_NULL
+    assert te(L, FAKE, FAKE + 4, None) == _lib.MOE_ERR_ALIGN
+    assert te(_layer(H=100), FAKE, FAKE, None) == _lib.MOE_ERR_SHAPE
+    L.experts_tiled = 1
+    assert te(L, FAKE, FAKE, None) == _lib.MOE_ERR_SHAPE and "already" in _lib.last_error()
+    assert _validate(L) == _lib.MOE_OK
+    L.experts_tiled = 3
+    assert _validate(L) == _lib.MOE_ERR_SHAPE and "experts_tiled" in _lib.last_error()
