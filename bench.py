@@ -26,11 +26,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
-DEFAULTS = {  # workload -> (steps, warmup, layers rotated)
-    "decode1": (2000, 100, 8),
-    "decode64": (200, 20, 2),
-    "prefill4096": (50, 5, 2),
-    "zipf16384": (20, 3, 2),
+# workload -> (steps, warmup, layers rotated).  The warm-up is ~0.1-0.2 s of
+# steps: shorter ones leave the GPU below its working clock for part of the
+# timed region (prefill4096 measured 8 % slower after 5 warm-up steps than
+# after 200).
+DEFAULTS = {
+    "decode1": (2000, 5000, 8),
+    "decode64": (200, 500, 2),
+    "prefill4096": (50, 300, 2),
+    "zipf16384": (20, 100, 2),
 }
 
 
