@@ -45,6 +45,7 @@
 // block, run side by side in one XCD and share them through its L2.
 #include "kernels.hpp"
 
+#include <type_traits>
 #include <utility>
 
 namespace moe {
@@ -85,8 +86,17 @@ __device__ __forceinline__ void lds_read_group(u32x4 (&a)[5], uint32_t addr, std
 __device__ __forceinline__ void wait_lds(u32x4 (&a)[5]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]) : : "memory");
 }
+// s_waitcnt vmcnt(N) through the builtin, which the compiler's own wait
+// insertion takes into account (it cannot see inside inline asm, and would
+// otherwise add a wait for zero outstanding loads before the first use of a
+// weight register in every unrolled iteration).  gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima.
 template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -229,15 +239,17 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
   issue(wb[0], 0, 0);
   issue(wb[1], 1, 1);
   issue(wb[2], 2, 2);
-  auto step = [&](u32x4 (&wcur)[2][2], u32x4 (&wnext)[2][2], int st, int ks) {
-    // This step's loads must have landed; younger are the loads of the later
-    // steps already issued (at most two), kVmPerStep per step and wave.
-    const int younger = min(2, nsteps - 1 - ks);
-    if (younger == 2) wait_vm<2 * kVmPerStep>();
-    else if (younger == 1) wait_vm<kVmPerStep>();
-    else wait_vm<0>();
+  // One k-step.  YOUNGER: loads of later steps already issued when this one
+  // starts (two, except in the last two steps), kVmPerStep per step and wave;
+  // ISSUE: whether this step requests step ks + 3.  Both are compile-time
+  // constants so that the compiler's own wait insertion sees straight-line
+  // counts (with a run-time condition it adds a wait for zero outstanding
+  // loads before the first use of a weight register in every iteration).
+  auto step = [&](auto younger_c, auto issue_c, u32x4 (&wcur)[2][2], u32x4 (&wnext)[2][2], int st, int ks) {
+    constexpr int YOUNGER = decltype(younger_c)::value;
+    wait_vm<YOUNGER * kVmPerStep>();   // this step's loads have landed
     barrier();   // every wave's part of the stage is in LDS; the stage read last step is free
-    if (ks + 3 < nsteps) issue(wnext, (st + 3) % NS, ks + 3);
+    if constexpr (decltype(issue_c)::value) issue(wnext, (st + 3) % NS, ks + 3);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t sa = lds_base + st * kATile + l16 * 128 + (((2 * q + h) ^ (l16 & 7)) << 4);
@@ -263,12 +275,24 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
     }
   };
   static_assert(NS == 4, "the loop below is unrolled for four slots");
-  for (int k4 = 0; k4 < nsteps; k4 += NS) {
-    step(wb[0], wb[3], 0, k4);
-    step(wb[1], wb[0], 1, k4 + 1);
-    step(wb[2], wb[1], 2, k4 + 2);
-    step(wb[3], wb[2], 3, k4 + 3);
+  using c0 = std::integral_constant<int, 0>;
+  using c1 = std::integral_constant<int, 1>;
+  using c2 = std::integral_constant<int, 2>;
+  using yes = std::true_type;
+  using no = std::false_type;
+  int k4 = 0;
+  for (; k4 + NS < nsteps; k4 += NS) {
+    step(c2{}, yes{}, wb[0], wb[3], 0, k4);
+    step(c2{}, yes{}, wb[1], wb[0], 1, k4 + 1);
+    step(c2{}, yes{}, wb[2], wb[1], 2, k4 + 2);
+    step(c2{}, yes{}, wb[3], wb[2], 3, k4 + 3);
   }
+  // The last four steps (nsteps is a multiple of four): only the first
+  // requests a later step.
+  step(c2{}, yes{}, wb[0], wb[3], 0, k4);
+  step(c2{}, no{}, wb[1], wb[0], 1, k4 + 1);
+  step(c1{}, no{}, wb[2], wb[1], 2, k4 + 2);
+  step(c0{}, no{}, wb[3], wb[2], 3, k4 + 3);
 
   // ---- epilogue: D[4 (lane / 16) + i][lane % 16] of each 16 x 16 block ----
   // All loads have landed (the last step waited for zero outstanding); every
