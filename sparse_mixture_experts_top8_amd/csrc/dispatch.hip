@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
 }
 
 // One workgroup per group (E: the shared expert): the descriptors of its
-// tiles in both grouped GEMMs, column tile major, row tile minor.
+// tiles in both grouped GEMMs, in gemm_tile_order.
 __global__ __launch_bounds__(256) void dispatch_tiles_kernel(LayerArgs L, int T, Work w) {
   const int g = blockIdx.x, E = L.E;
   const bool shared = g == E;
@@ -96,11 +96,13 @@ __global__ __launch_bounds__(256) void dispatch_tiles_kernel(LayerArgs L, int T,
   const int ngu = (2 * (shared ? L.Is : L.I) + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
   const int bgu = w.tiles_gu[g], bdn = w.tiles_dn[g];
   for (int i = threadIdx.x; i < mt * ngu; i += 256) {
-    const int nt = i / mt, mi = i - nt * mt;
+    int mi, nt;
+    gemm_tile_order(i, mt, ngu, mi, nt);
     w.tdesc_gu[bgu + i] = make_int4(g, seg0, nrows, mi | (nt << 16));
   }
   for (int i = threadIdx.x; i < mt * ndn; i += 256) {
-    const int nt = i / mt, mi = i - nt * mt;
+    int mi, nt;
+    gemm_tile_order(i, mt, ndn, mi, nt);
     w.tdesc_dn[bdn + i] = make_int4(g, seg0, nrows, mi | (nt << 16));
   }
 }
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
     w.tiles_gu[g] = s_tgu[g];
     w.tiles_dn[g] = s_tdn[g];
   }
-  // Tile descriptors, one thread per group (column tile major).
+  // Tile descriptors, one thread per group (gemm_tile_order).
   if (tid <= E) {
     const int g = tid;
     const bool shared = g == E;
@@ -207,11 +209,17 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
     const int mt = (nrows + kGemmBM - 1) / kGemmBM;
     const int ngu = (2 * (shared ? L.Is : L.I) + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
     int4* gu = w.tdesc_gu + s_tgu[g];
-    for (int nt = 0; nt < ngu; ++nt)
-      for (int mi = 0; mi < mt; ++mi) *gu++ = make_int4(g, seg0, nrows, mi | (nt << 16));
+    for (int i = 0; i < mt * ngu; ++i) {
+      int mi, nt;
+      gemm_tile_order(i, mt, ngu, mi, nt);
+      gu[i] = make_int4(g, seg0, nrows, mi | (nt << 16));
+    }
     int4* dn = w.tdesc_dn + s_tdn[g];
-    for (int nt = 0; nt < ndn; ++nt)
-      for (int mi = 0; mi < mt; ++mi) *dn++ = make_int4(g, seg0, nrows, mi | (nt << 16));
+    for (int i = 0; i < mt * ndn; ++i) {
+      int mi, nt;
+      gemm_tile_order(i, mt, ndn, mi, nt);
+      dn[i] = make_int4(g, seg0, nrows, mi | (nt << 16));
+    }
   }
   // Scatter.
   for (int q = tid; q < TK; q += kSmallThreads) {

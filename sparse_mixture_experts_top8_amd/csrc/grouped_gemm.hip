@@ -40,9 +40,10 @@
 //
 // Scheduling: workgroups are handed to the eight XCDs round-robin (workgroup i
 // on XCD i % 8); the tile list is cut into eight contiguous ranges and XCD x
-// takes range x in order.  Tiles are ordered (group, column tile, row tile): a
-// group's row tiles of one weight slab, and its column tiles of one activation
-// block, run side by side in one XCD and share them through its L2.
+// takes range x in order.  Within a group, tiles come in blocks of eight row
+// tiles, column tile major inside a block (gemm_tile_order): a block's row
+// tiles of one weight slab, and its column tiles of one activation block, run
+// side by side in one XCD and share them through its L2.
 #include "kernels.hpp"
 
 #include <type_traits>

@@ -18,6 +18,29 @@ __host__ __device__ inline int64_t gemm_tile_bound(int64_t T, int K, int E, int 
   return ((T * K + kGemmBM - 1) / kGemmBM + E) * nt + ((T + kGemmBM - 1) / kGemmBM) * nts;
 }
 
+// Order of a group's mt x nct tiles in the dispatch list: blocks of
+// kGemmRowBlock row tiles, within a block column tile major and row tile
+// minor.  Consecutive tiles run side by side on one XCD, so a block's
+// activation rows are fetched once for all its column tiles and its weight
+// columns once for all its row tiles (through that XCD's L2); a group of at
+// most kGemmRowBlock row tiles is simply column tile major.
+constexpr int kGemmRowBlock = 8;
+__host__ __device__ inline void gemm_tile_order(int i, int mt, int nct, int& mi, int& nt) {
+  const int full = (mt / kGemmRowBlock) * kGemmRowBlock * nct;   // tiles of the full row blocks
+  int b, rows, j;
+  if (i < full) {
+    b = i / (kGemmRowBlock * nct);
+    rows = kGemmRowBlock;
+    j = i - b * kGemmRowBlock * nct;
+  } else {
+    b = mt / kGemmRowBlock;
+    rows = mt - b * kGemmRowBlock;
+    j = i - full;
+  }
+  nt = j / rows;
+  mi = b * kGemmRowBlock + (j - nt * rows);
+}
+
 __host__ __device__ inline int router_blocks(int64_t T) { return (int)((T + kRouterTokens - 1) / kRouterTokens); }
 // Columns of a row of router partial sums: E logits, the shared gate, padding
 // to a multiple of 4.
