@@ -85,10 +85,10 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
   }
 }
 
-// One workgroup per group (E: the shared expert): the descriptors of its
-// tiles in both grouped GEMMs, in gemm_tile_order.
-__global__ __launch_bounds__(256) void dispatch_tiles_kernel(LayerArgs L, int T, Work w) {
-  const int g = blockIdx.x, E = L.E;
+// Workgroup g of the group tiles (E: the shared expert): the descriptors of
+// its tiles in both grouped GEMMs, in gemm_tile_order.
+__device__ void dispatch_tiles(LayerArgs L, int T, const Work& w, int g) {
+  const int E = L.E;
   const bool shared = g == E;
   const int seg0 = shared ? 0 : w.offsets[g];
   const int nrows = shared ? T : w.offsets[g + 1] - seg0;
@@ -107,12 +107,12 @@ __global__ __launch_bounds__(256) void dispatch_tiles_kernel(LayerArgs L, int T,
   }
 }
 
-// Stable scatter of one router block's pairs (at most 32*K <= 256).
-__global__ __launch_bounds__(256) void dispatch_scatter_kernel(LayerArgs L, int T, Work w) {
+// Stable scatter of router block blk's pairs (at most 32*K <= 256).
+__device__ void dispatch_scatter(LayerArgs L, int T, const Work& w, int blk) {
   __shared__ int keys[256];
   const int E = L.E, K = L.K;
   const int j = threadIdx.x;
-  const int q0 = blockIdx.x * kRouterTokens * K;
+  const int q0 = blk * kRouterTokens * K;
   const int n = min(kRouterTokens * K, T * K - q0);
   const int key = j < n ? w.topk_idx[q0 + j] : -1;
   keys[j] = key;
@@ -120,11 +120,20 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(LayerArgs L, int 
   if (j < n) {
     int rank = 0;
     for (int i = 0; i < j; ++i) rank += (keys[i] == key);
-    const int slot = w.offsets[key] + w.blk_counts[(size_t)blockIdx.x * E + key] + rank;
+    const int slot = w.offsets[key] + w.blk_counts[(size_t)blk * E + key] + rank;
     w.perm[slot] = q0 + j;
     w.slot_of[q0 + j] = slot;
     w.slot_tok[slot] = (q0 + j) / K;
   }
+}
+
+// Tile descriptors and the scatter depend only on the offsets, tile prefix
+// sums and block bases, so they share one launch: workgroups 0 .. E write the
+// groups' tile descriptors, the rest scatter one router block each.
+__global__ __launch_bounds__(256) void dispatch_place_kernel(LayerArgs L, int T, Work w) {
+  const int b = blockIdx.x;
+  if (b <= L.E) dispatch_tiles(L, T, w, b);
+  else dispatch_scatter(L, T, w, b - (L.E + 1));
 }
 
 // Batches of at most kSmallBlocks router blocks: the whole dispatch in one
@@ -241,8 +250,7 @@ hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t
   }
   hipLaunchKernelGGL(dispatch_count_kernel, dim3(L.E), dim3(256), 0, s, L, T, w);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, s, L, T, w);
-  hipLaunchKernelGGL(dispatch_tiles_kernel, dim3(L.E + 1), dim3(256), 0, s, L, T, w);
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(router_blocks(T)), dim3(256), 0, s, L, T, w);
+  hipLaunchKernelGGL(dispatch_place_kernel, dim3(L.E + 1 + router_blocks(T)), dim3(256), 0, s, L, T, w);
   return hipGetLastError();
 }
 
