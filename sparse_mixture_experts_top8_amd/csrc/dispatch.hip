@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(LayerArgs L, int T,
 // block's pairs of that expert is the population of the mask below its
 // token (tokens of a block are distinct per expert, and pair ids grow with
 // the token), so the slots equal those of the multi-kernel path.
-constexpr int kSmallBlocks = 64;
+constexpr int kSmallBlocks = kDispatchSmallBlocks;
 constexpr int kSmallThreads = 1024;
 
 __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs L, int T, Work w) {
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
 }  // namespace
 
 hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s) {
-  if (router_blocks(T) <= kSmallBlocks) {
+  if (dispatch_single_block(T)) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallThreads), 0, s, L, T, w);
     return hipGetLastError();
   }

@@ -42,6 +42,10 @@ __host__ __device__ inline void gemm_tile_order(int i, int mt, int nct, int& mi,
 }
 
 __host__ __device__ inline int router_blocks(int64_t T) { return (int)((T + kRouterTokens - 1) / kRouterTokens); }
+// Batches of at most this many router blocks are dispatched by one workgroup,
+// which builds its own token masks (no per-block histograms needed).
+constexpr int kDispatchSmallBlocks = 64;
+__host__ __device__ inline bool dispatch_single_block(int64_t T) { return router_blocks(T) <= kDispatchSmallBlocks; }
 // Columns of a row of router partial sums: E logits, the shared gate, padding
 // to a multiple of 4.
 __host__ __device__ inline int router_cols(int E) { return (E + 1 + 3) & ~3; }

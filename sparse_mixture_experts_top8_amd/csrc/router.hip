@@ -22,7 +22,10 @@
 // re-reads through L2, not the arithmetic, set the kernel's pace.  Small batches split H into up
 // to H/64 slices so that the launch still spans the chip.
 // router_select_kernel: one workgroup of 16 waves per 32 tokens sums the
-// slices in a fixed order and selects, two tokens per wave.
+// slices in a fixed order and selects, two tokens per wave, and writes the
+// block histograms of the multi-launch dispatch; batches small enough for
+// the one-workgroup dispatch use router_select_tok_kernel (one wave per
+// token, no histograms).
 #include "kernels.hpp"
 
 namespace moe {
@@ -213,6 +216,58 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs
   }
 }
 
+// Batches whose dispatch runs in one workgroup (dispatch_single_block) need
+// no per-block histograms, so the selection is spread over the chip instead:
+// one wave per token, four tokens per workgroup.  Lane l holds columns
+// 4 l .. 4 l + 3 (the top-K's layout), summed over the slices in the same
+// order as router_select_kernel, so the results are the same bit for bit.
+__global__ __launch_bounds__(256) void router_select_tok_kernel(LayerArgs L, int T, int ksplit,
+                                                                const float* __restrict__ part, Work w,
+                                                                float* __restrict__ logits_out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;   // the whole wave; no barrier below
+  const int E = L.E, K = L.K, Ep = router_cols(E);
+  const float* src = part + (size_t)t * Ep;
+  const size_t sstride = (size_t)T * Ep;
+  const bool have = 4 * lane < Ep;
+  u32x4 q[kMaxSlices];
+  float g[kMaxSlices];
+#pragma unroll
+  for (int i = 0; i < kMaxSlices; ++i)
+    if (i < ksplit) {
+      q[i] = have ? ld16(src + i * sstride + 4 * lane) : u32x4{0u, 0u, 0u, 0u};
+      g[i] = src[i * sstride + E];
+    }
+  float lv[1][4] = {{0.f, 0.f, 0.f, 0.f}};
+  float zg = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxSlices; ++i)
+    if (i < ksplit) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lv[0][c] += __uint_as_float(q[i][c]);
+      zg += g[i];
+    }
+  if (L.logits_bf16) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) lv[0][c] = round_bf16(lv[0][c]);
+    zg = round_bf16(zg);
+  }
+  if (lane == 0) w.gate_s[t] = sigmoidf_(zg);
+  if (logits_out) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (4 * lane + c < E) logits_out[(size_t)t * E + 4 * lane + c] = lv[0][c];
+  }
+  int ix[1];
+  float wv[1];
+  topk_select<1>(lv, E, K, lane, ix, wv);
+  if (lane < K) {
+    w.topk_idx[(size_t)t * K + lane] = ix[0];
+    w.topk_w[(size_t)t * K + lane] = wv[0];
+  }
+}
+
 // Full stable ranking of each row's scores: rank[e] = the number of experts
 // that score higher, plus those that score the same with a lower index.  One
 // wave per row.  Each expert gets the 64-bit key (order-preserving score key,
@@ -323,8 +378,12 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
     hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(router_select_kernel, dim3(router_blocks(T)), dim3(kSelWaves * 64), 0, s, L, T, ks,
-                     (const float*)w.rlog, w, logits_out, psum_out);
+  if (!psum_out && dispatch_single_block(T))
+    hipLaunchKernelGGL(router_select_tok_kernel, dim3((T + 3) / 4), dim3(256), 0, s, L, T, ks, (const float*)w.rlog,
+                       w, logits_out);
+  else
+    hipLaunchKernelGGL(router_select_kernel, dim3(router_blocks(T)), dim3(kSelWaves * 64), 0, s, L, T, ks,
+                       (const float*)w.rlog, w, logits_out, psum_out);
   return hipGetLastError();
 }
 
