@@ -21,11 +21,12 @@
 // slice).  For large batches the router is read once per 64 tokens: its
 // re-reads through L2, not the arithmetic, set the kernel's pace.  Small batches split H into up
 // to H/64 slices so that the launch still spans the chip.
-// router_select_kernel: one workgroup of 16 waves per 32 tokens sums the
-// slices in a fixed order and selects, two tokens per wave, and writes the
-// block histograms of the multi-launch dispatch; batches small enough for
-// the one-workgroup dispatch use router_select_tok_kernel (one wave per
-// token, no histograms).
+// router_select_kernel (for the load-balance statistic, which needs its
+// per-block probability sums): one workgroup of 16 waves per 32 tokens sums
+// the slices in a fixed order and selects, two tokens per wave, and writes
+// the block histograms of the multi-launch dispatch;
+// everything else uses router_select_tok_kernel (one wave per token; block
+// histograms by integer atomics where the dispatch needs them).
 #include "kernels.hpp"
 
 namespace moe {
@@ -41,8 +42,15 @@ constexpr int kMaxRouterCols = 260;      // router_cols(256)
 // kTB 16-token blocks per workgroup.
 template <int kTB>
 __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
-                                                            int ksplit, float* __restrict__ part) {
+                                                            int ksplit, float* __restrict__ part,
+                                                            int* __restrict__ hist_zero, int hist_n) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // The selection adds its pairs to these block histograms (integer atomics):
+  // they start at zero.
+  if (hist_zero) {
+    const int nwg = gridDim.x * gridDim.y, wg = blockIdx.y * gridDim.x + blockIdx.x;
+    for (int i = wg * 256 + tid; i < hist_n; i += nwg * 256) hist_zero[i] = 0;
+  }
   const int t0 = blockIdx.x * 16 * kTB, s = blockIdx.y;
   const int H = L.H, E = L.E, Ep = router_cols(E);
   const int nsub = (E + 1 + 15) >> 4;               // column blocks incl. the gate column
@@ -216,14 +224,15 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs
   }
 }
 
-// Batches whose dispatch runs in one workgroup (dispatch_single_block) need
-// no per-block histograms, so the selection is spread over the chip instead:
-// one wave per token, four tokens per workgroup.  Lane l holds columns
-// 4 l .. 4 l + 3 (the top-K's layout), summed over the slices in the same
-// order as router_select_kernel, so the results are the same bit for bit.
+// The selection spread over the chip: one wave per token, four tokens per
+// workgroup.  Lane l holds columns 4 l .. 4 l + 3 (the top-K's layout),
+// summed over the slices in the same order as router_select_kernel, so the
+// results are the same bit for bit.  For the multi-launch dispatch
+// (block_hist) each selected pair is counted into its router block's
+// histogram, which the logits kernel zeroed.
 __global__ __launch_bounds__(256) void router_select_tok_kernel(LayerArgs L, int T, int ksplit,
                                                                 const float* __restrict__ part, Work w,
-                                                                float* __restrict__ logits_out) {
+                                                                float* __restrict__ logits_out, int block_hist) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;   // the whole wave; no barrier below
@@ -265,6 +274,9 @@ __global__ __launch_bounds__(256) void router_select_tok_kernel(LayerArgs L, int
   if (lane < K) {
     w.topk_idx[(size_t)t * K + lane] = ix[0];
     w.topk_w[(size_t)t * K + lane] = wv[0];
+    // The multi-launch dispatch takes per-block expert histograms; integer
+    // sums do not depend on the order of the additions.
+    if (block_hist) atomicAdd(&w.blk_counts[(size_t)(t / kTok) * E + ix[0]], 1);
   }
 }
 
@@ -372,15 +384,21 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
                          float* logits_out, hipStream_t s, float* psum_out) {
   const int ks = router_ksplit(T, L.H), tile = logits_tile(T);
   const dim3 grid((T + tile - 1) / tile, ks);
+  // Per-token selection unless the load-balance statistic's block sums are
+  // wanted; its block histograms (multi-launch dispatch only) start at zero.
+  const bool per_token = psum_out == nullptr;
+  const bool block_hist = per_token && !dispatch_single_block(T);
+  int* hz = block_hist ? w.blk_counts : nullptr;
+  const int hn = router_blocks(T) * L.E;
   if (tile == 32)
-    hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog);
+    hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn);
   else
-    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog);
+    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!psum_out && dispatch_single_block(T))
+  if (per_token)
     hipLaunchKernelGGL(router_select_tok_kernel, dim3((T + 3) / 4), dim3(256), 0, s, L, T, ks, (const float*)w.rlog,
-                       w, logits_out);
+                       w, logits_out, block_hist ? 1 : 0);
   else
     hipLaunchKernelGGL(router_select_kernel, dim3(router_blocks(T)), dim3(kSelWaves * 64), 0, s, L, T, ks,
                        (const float*)w.rlog, w, logits_out, psum_out);
