@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--row-major", action="store_true",
                     help="keep the routed experts row-major instead of the MFMA-tile layout")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="skip the other entry points' timings (load balance, sub-block, bf16 scores, streamed "
+                         "experts), so that a kernel trace holds the layer's own launches")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -134,6 +137,61 @@ def measured_traffic(workload, kernel):
     for f in (rec["source"], "common.hpp", "kernels.hpp"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return int(rec["traffic_bytes"]) if h.hexdigest()[:16] == rec["source_sha"] else None
+
+
+def other_entry_points(moe, mi, d, wl, T, steps, warmup, nlayers, layers, xs, outs, ws, time_calls):
+    """Timings of the other entry points on the same batches: the load-balance
+    statistic, the sub-block form, bf16 router scores (and ranks), and routed
+    experts streamed from pinned host memory."""
+    import numpy as np
+    import torch
+    # Load-balance statistic of the same batches (moe_load_balance: router,
+    # dispatch and the statistic), timed outside the step.
+    lb_steps = min(steps, 200)
+    lb_out = [moe.load_balance(xs[l], layers[l], ws=ws) for l in range(nlayers)]
+    load_balance = {
+        "us_per_call": time_calls(lambda i: moe.load_balance(xs[i % nlayers], layers[i % nlayers], ws=ws), lb_steps),
+        "lb": round(float(np.mean([float(r["lb"].item()) for r in lb_out])), 6),
+        "definition": "E * sum_e f_e * P_e (slot fraction x mean full-softmax probability)"}
+
+    # The sub-block form out = h + layer(RMSNorm(h)) on the same batches.
+    norm_w = moe.bits_to_device(
+        mi.f32_to_bf16_bits(np.random.default_rng(11).normal(1.0, 0.2, d.H).astype(np.float32)), "cuda")
+    block = {"us_per_call": time_calls(lambda i: moe.block_forward(xs[i % nlayers], layers[i % nlayers], norm_w,
+                                                                   1e-6, out=outs[i % nlayers], ws=ws),
+                                       lb_steps, min(warmup, 20)),
+             "definition": "out = h + layer(RMSNorm(h)), eps 1e-6"}
+
+    # The layer with bf16 router scores (logits_bf16) on the same batches, and
+    # the stable ranks of one batch's [T, E] scores.
+    layers_b = [ly.with_logits_bf16() for ly in layers]
+    logits_b = moe.route(xs[0], layers_b[0], ws=ws, want_logits=True)["logits"]
+    bf16_logits = {
+        "us_per_call": time_calls(lambda i: moe.forward(xs[i % nlayers], layers_b[i % nlayers],
+                                                        out=outs[i % nlayers], ws=ws), lb_steps, min(warmup, 20)),
+        "ranks_us_per_call": time_calls(lambda i: moe.ranks(logits_b), lb_steps, 5),
+        "definition": "router and shared-gate scores rounded to bf16; ranks of [T, E] fp32 scores"}
+
+    # Routed experts streamed from pinned host memory (moe_forward_streamed)
+    # into a device cache big enough for one round; the bytes that cross the
+    # host link per call are the touched experts' weights.
+    host_params = dict(layers[0].params)
+    host_params["gate_up_proj"] = host_params["gate_up_proj"].cpu().pin_memory()
+    host_params["down_proj"] = host_params["down_proj"].cpu().pin_memory()
+    host_layer = moe.MoeLayer(d.H, d.E, d.K, d.I, d.Is, host_params, False, layers[0].experts_tiled)
+    cache = moe.expert_cache(host_layer, min(d.E, T * d.K))
+    U_host = [int((torch.bincount(moe.route(x, layers[0], ws=ws)["topk_idx"].view(-1).long(),
+                                  minlength=d.E) > 0).sum()) for x in xs]
+    st_calls = 20 if T <= 16 else 4
+    st_us = time_calls(lambda i: moe.forward_streamed(xs[i % nlayers], host_layer, cache, out=outs[i % nlayers],
+                                                      ws=ws), st_calls, 2)
+    st_bytes = float(np.mean([U_host[i % nlayers] for i in range(st_calls)])) * 3 * d.H * d.I * 2
+    streamed = {"us_per_call": st_us, "slots": min(d.E, T * d.K),
+                "host_bytes_per_call": int(st_bytes),
+                "host_link_GBps": round(st_bytes / (st_us * 1e-6) / 1e9, 2),
+                "definition": "routed experts' weights in pinned host memory, touched ones copied per call"}
+    del host_params, host_layer, cache
+    return load_balance, block, bf16_logits, streamed
 
 
 def step_work(d, T, U):
@@ -251,52 +309,10 @@ def main():
         torch.cuda.synchronize()
         return round(start.elapsed_time(end) / n * 1e3, 2)
 
-    # Load-balance statistic of the same batches (moe_load_balance: router,
-    # dispatch and the statistic), timed outside the step.
-    lb_steps = min(steps, 200)
-    lb_out = [moe.load_balance(xs[l], layers[l], ws=ws) for l in range(nlayers)]
-    load_balance = {
-        "us_per_call": time_calls(lambda i: moe.load_balance(xs[i % nlayers], layers[i % nlayers], ws=ws), lb_steps),
-        "lb": round(float(np.mean([float(r["lb"].item()) for r in lb_out])), 6),
-        "definition": "E * sum_e f_e * P_e (slot fraction x mean full-softmax probability)"}
-
-    # The sub-block form out = h + layer(RMSNorm(h)) on the same batches.
-    norm_w = moe.bits_to_device(
-        mi.f32_to_bf16_bits(np.random.default_rng(11).normal(1.0, 0.2, d.H).astype(np.float32)), "cuda")
-    block = {"us_per_call": time_calls(lambda i: moe.block_forward(xs[i % nlayers], layers[i % nlayers], norm_w,
-                                                                   1e-6, out=outs[i % nlayers], ws=ws),
-                                       lb_steps, min(warmup, 20)),
-             "definition": "out = h + layer(RMSNorm(h)), eps 1e-6"}
-
-    # The layer with bf16 router scores (logits_bf16) on the same batches, and
-    # the stable ranks of one batch's [T, E] scores.
-    layers_b = [ly.with_logits_bf16() for ly in layers]
-    logits_b = moe.route(xs[0], layers_b[0], ws=ws, want_logits=True)["logits"]
-    bf16_logits = {
-        "us_per_call": time_calls(lambda i: moe.forward(xs[i % nlayers], layers_b[i % nlayers],
-                                                        out=outs[i % nlayers], ws=ws), lb_steps, min(warmup, 20)),
-        "ranks_us_per_call": time_calls(lambda i: moe.ranks(logits_b), lb_steps, 5),
-        "definition": "router and shared-gate scores rounded to bf16; ranks of [T, E] fp32 scores"}
-
-    # Routed experts streamed from pinned host memory (moe_forward_streamed)
-    # into a device cache big enough for one round; the bytes that cross the
-    # host link per call are the touched experts' weights.
-    host_params = dict(layers[0].params)
-    host_params["gate_up_proj"] = host_params["gate_up_proj"].cpu().pin_memory()
-    host_params["down_proj"] = host_params["down_proj"].cpu().pin_memory()
-    host_layer = moe.MoeLayer(d.H, d.E, d.K, d.I, d.Is, host_params, False, layers[0].experts_tiled)
-    cache = moe.expert_cache(host_layer, min(d.E, T * d.K))
-    U_host = [int((torch.bincount(moe.route(x, layers[0], ws=ws)["topk_idx"].view(-1).long(),
-                                  minlength=d.E) > 0).sum()) for x in xs]
-    st_calls = 20 if T <= 16 else 4
-    st_us = time_calls(lambda i: moe.forward_streamed(xs[i % nlayers], host_layer, cache, out=outs[i % nlayers],
-                                                      ws=ws), st_calls, 2)
-    st_bytes = float(np.mean([U_host[i % nlayers] for i in range(st_calls)])) * 3 * d.H * d.I * 2
-    streamed = {"us_per_call": st_us, "slots": min(d.E, T * d.K),
-                "host_bytes_per_call": int(st_bytes),
-                "host_link_GBps": round(st_bytes / (st_us * 1e-6) / 1e9, 2),
-                "definition": "routed experts' weights in pinned host memory, touched ones copied per call"}
-    del host_params, host_layer, cache
+    load_balance = block = bf16_logits = streamed = None
+    if not args.layer_only:
+        load_balance, block, bf16_logits, streamed = other_entry_points(moe, mi, d, wl, T, steps, warmup, nlayers,
+                                                                        layers, xs, outs, ws, time_calls)
 
     # Kernel attribution: the same steps again, each recording six events at
     # its phase boundaries on the same stream (the fused decode path records
