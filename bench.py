@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--layer-only", action="store_true",
                     help="skip the other entry points' timings (load balance, sub-block, bf16 scores, streamed "
                          "experts), so that a kernel trace holds the layer's own launches")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="only time moe_forward at batch sizes 1..64 (the full-shape layer, 8 layers rotated) and "
+                         "print one JSON line per size")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -71,6 +74,42 @@ def copy_probe():
     torch.cuda.synchronize()
     log(f"copy probe: 5 copies of {n} bytes ({n // 1024} KiB read and written per copy)")
     print(json.dumps({"copy_probe_bytes": n}))
+
+
+def batch_sweep():
+    """Step time of the layer at batch sizes 1..64 on either side of the
+    fused-decode / grouped-path switch (T <= 16 / T > 16): 8 full-shape layers
+    rotated (tiled experts), x ~ N(0, 1) seeded by T, 400 warm-up and 400 timed
+    calls; bytes = touched experts once + shared expert + router + x and out."""
+    import numpy as np
+    import torch
+    import moe_inputs as mi
+    import sparse_mixture_experts_top8_amd as moe
+    wl = mi.WORKLOADS["decode64"]
+    d = wl.dims
+    base = mi.workload_layer(wl)
+    layers = [device_layer(moe, mi, wl, l, base).tiled() for l in range(8)]
+    for T in [1, 2, 4, 8, 12, 16, 17, 24, 32, 48, 64]:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(T)
+        xs = [torch.randn((T, d.H), generator=g, device="cuda").to(torch.bfloat16) for _ in range(8)]
+        outs = [torch.empty_like(x) for x in xs]
+        ws = layers[0].workspace(T)
+        for i in range(400):
+            moe.forward(xs[i % 8], layers[i % 8], out=outs[i % 8], ws=ws)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(400):
+            moe.forward(xs[i % 8], layers[i % 8], out=outs[i % 8], ws=ws)
+        e.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) / 400 * 1e3
+        U = float(np.mean([int((torch.bincount(moe.route(xs[l], layers[l], ws=ws)["topk_idx"].view(-1).long(),
+                                               minlength=d.E) > 0).sum()) for l in range(8)]))
+        nbytes, _ = step_work(d, T, U)
+        print(json.dumps({"T": T, "path": "fused decode" if T <= 16 else "grouped", "us_per_step": round(us, 2),
+                          "experts_touched": U, "alg_TBps": round(nbytes / us / 1e6, 3)}), flush=True)
 
 
 def device_layer(moe, mi, wl, l, base_bits):
@@ -239,6 +278,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is measured on a "
               f"single MI355X and no multi-GPU path exists", file=sys.stderr)
         sys.exit(2)
+    if args.batch_sweep:
+        batch_sweep()
+        return
     if args.copy_probe:
         return copy_probe()
 
