@@ -217,17 +217,16 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
     const int nrows = shared ? T : s_cnt[g];
     const int mt = (nrows + kGemmBM - 1) / kGemmBM;
     const int ngu = (2 * (shared ? L.Is : L.I) + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
+    // gemm_tile_order as nested loops (one thread writes all of a group's
+    // descriptors: no divisions on that serial path).
     int4* gu = w.tdesc_gu + s_tgu[g];
-    for (int i = 0; i < mt * ngu; ++i) {
-      int mi, nt;
-      gemm_tile_order(i, mt, ngu, mi, nt);
-      gu[i] = make_int4(g, seg0, nrows, mi | (nt << 16));
-    }
     int4* dn = w.tdesc_dn + s_tdn[g];
-    for (int i = 0; i < mt * ndn; ++i) {
-      int mi, nt;
-      gemm_tile_order(i, mt, ndn, mi, nt);
-      dn[i] = make_int4(g, seg0, nrows, mi | (nt << 16));
+    for (int b0 = 0; b0 < mt; b0 += kGemmRowBlock) {
+      const int rows = min(kGemmRowBlock, mt - b0);
+      for (int nt = 0; nt < ngu; ++nt)
+        for (int r = 0; r < rows; ++r) *gu++ = make_int4(g, seg0, nrows, (b0 + r) | (nt << 16));
+      for (int nt = 0; nt < ndn; ++nt)
+        for (int r = 0; r < rows; ++r) *dn++ = make_int4(g, seg0, nrows, (b0 + r) | (nt << 16));
     }
   }
   // Scatter.
