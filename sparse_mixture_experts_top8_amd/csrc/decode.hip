@@ -74,8 +74,8 @@ constexpr int kCtlError = 0;             // 0, or the call's tag once one of its
 constexpr int kCtlFlags = 32;            // + x * kDecodeFlagStride: copy x of the arrival flags
 static_assert(kDecodeCtlWords >= kCtlFlags + kDecodeReplicas * kDecodeFlagStride, "control block too small");
 
-// Weight fragment (plain load: on MI355X the non-temporal hint measured
-// slower for these streams).
+// Phase A weight fragment (plain load: the non-temporal hint measured slower
+// here, 21.1 against 20.2 us at one token).
 __device__ __forceinline__ u32x4 ldw(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 ld_lds16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -116,6 +116,13 @@ __device__ __forceinline__ u32x4 ld_after16(rsrc_t r, uint32_t off) {
 // load counter then matches in every path) and add zero.
 __device__ __forceinline__ u32x4 ldw_buf(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+// The same, non-temporal (cache policy bit 1): the routed gate/up stream of
+// phase B, read once per call and by one workgroup, stays out of the caches
+// (one token: 21.6 -> 20.2 us).  The down-projection stream measured slower
+// with the hint (20.7 us with both) and keeps plain loads.
+__device__ __forceinline__ u32x4 ldw_buf_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
 }
 
 // All of this wave's earlier memory operations have completed (stores at the
@@ -529,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < kMaxHSteps; ++ks)
-        st[ks] = ldw_buf(r_gu, ks < nks ? off + ks2 * (uint32_t)(ks >> 1) + ks1 * (uint32_t)(ks & 1) : kOutside);
+        st[ks] = ldw_buf_nt(r_gu, ks < nks ? off + ks2 * (uint32_t)(ks >> 1) + ks1 * (uint32_t)(ks & 1) : kOutside);
     };
     auto compute = [&](u32x4 (&st)[kMaxHSteps], int i) {
       if (i < nmine) {
