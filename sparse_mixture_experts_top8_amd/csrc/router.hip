@@ -16,9 +16,9 @@
 // Two kernels.  router_logits_kernel: one workgroup per (64-token tile, or
 // 32-token tile for small batches, slice of H); the shared gate row rides along as column E, so the E + 1 columns
 // are 17 MFMA column blocks of 16.  Each wave streams its column blocks' rows
-// and the tile's x rows through a three-step register pipeline and writes
-// fp32 partial sums (one fp32 accumulator chain of at most H / 32 steps per
-// slice).  For large batches the router is read once per 64 tokens: its
+// and the tile's x rows through a two-step register pipeline of 64-wide
+// k-steps (each row's whole 128-byte line per step) and writes fp32 partial
+// sums (one fp32 accumulator chain of at most H / 32 MFMAs per slice).  For large batches the router is read once per 64 tokens: its
 // re-reads through L2, not the arithmetic, set the kernel's pace.  Small batches split H into up
 // to H/64 slices so that the launch still spans the chip.
 // router_select_kernel (for the load-balance statistic, which needs its
@@ -36,7 +36,7 @@ namespace {
 constexpr int kTok = kRouterTokens;      // 32 tokens per select block
 constexpr int kSmallT = 256;             // up to this many tokens: 32-token logits tiles, else 64
 constexpr int kColBlocks = 5;            // column blocks per wave (17 for E = 256, plus the gate column)
-constexpr int kDepth = 3;                // k-steps in flight per wave
+constexpr int kDepth = 2;                // 64-wide k-steps in flight per wave
 constexpr int kMaxRouterCols = 260;      // router_cols(256)
 
 // kTB 16-token blocks per workgroup.
@@ -54,8 +54,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
   const int t0 = blockIdx.x * 16 * kTB, s = blockIdx.y;
   const int H = L.H, E = L.E, Ep = router_cols(E);
   const int nsub = (E + 1 + 15) >> 4;               // column blocks incl. the gate column
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int klen = H / ksplit, kbeg = s * klen, nk = klen / 32;
+  // k advances 64 at a time; lane quarter q (lane / 16) covers elements
+  // 16 q .. 16 q + 15 of the step with two consecutive 16-byte loads (MFMA
+  // halves 0 and 1), the same order for both operands, so each row's whole
+  // 128-byte line is requested at once.
+  const int r16 = lane & 15, kq = (lane >> 4) * 16;
+  const int klen = H / ksplit, kbeg = s * klen, nk = klen / 64;
 
   // Operand rows of this lane: x rows of the 16-token blocks, weight rows of
   // the wave's column blocks (rows past T or E + 1 repeat a valid row and
@@ -75,15 +79,19 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
 #pragma unroll
     for (int jj = 0; jj < kColBlocks; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Ring of kDepth k-steps; loads of k-steps past the slice repeat its last
-  // step (always in bounds) and are not used.
-  u32x4 ra[kDepth][kTB], rb[kDepth][kColBlocks];
+  // Ring of kDepth 64-wide k-steps; loads of k-steps past the slice repeat
+  // its last step (always in bounds) and are not used.
+  u32x4 ra[kDepth][kTB][2], rb[kDepth][kColBlocks][2];
   auto issue = [&](int st, int ks) {
-    const int k = 32 * min(ks, nk - 1);
+    const int k = 64 * min(ks, nk - 1);
 #pragma unroll
-    for (int i = 0; i < kTB; ++i) ra[st][i] = ld16(arow[i] + k);
+    for (int i = 0; i < kTB; ++i)
 #pragma unroll
-    for (int jj = 0; jj < kColBlocks; ++jj) rb[st][jj] = ld16(brow[jj] + k);
+      for (int h = 0; h < 2; ++h) ra[st][i][h] = ld16(arow[i] + k + 8 * h);
+#pragma unroll
+    for (int jj = 0; jj < kColBlocks; ++jj)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) rb[st][jj][h] = ld16(brow[jj] + k + 8 * h);
   };
 #pragma unroll
   for (int st = 0; st < kDepth; ++st) issue(st, st);
@@ -96,9 +104,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
         for (int jj = 0; jj < kColBlocks; ++jj) {
           if (wave + 4 * jj < nsub) {
 #pragma unroll
-            for (int i = 0; i < kTB; ++i)
-              acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[st][i]), as_bf16x8(rb[st][jj]),
-                                                                   acc[i][jj], 0, 0, 0);
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < kTB; ++i)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[st][i][h]),
+                                                                     as_bf16x8(rb[st][jj][h]), acc[i][jj], 0, 0, 0);
           }
         }
       }
