@@ -134,10 +134,11 @@ int moe_route(const moe_layer_t *L, const void *x, int64_t T,
  *   mean_prob fp32 [E] or NULL   P_e
  *   counts    int32 [E] or NULL  pairs routed to each expert
  * Device pointers, 4-byte aligned; x bf16 [T, H] and the workspace (size from
- * moe_workspace_bytes) 16-byte aligned.  Uses the same router, top-K and
- * dispatch kernels as moe_forward for T > 16 at any T; sums are in a fixed
- * order, so repeated calls give identical results.  T = 0 is a successful
- * no-op.  Errors as moe_route. */
+ * moe_workspace_bytes) 16-byte aligned.  Routes with moe_forward's logits
+ * kernel for T > 16 (at any T), the same top-K rule and summation order
+ * (identical indices and weights) and the same dispatch kernels; sums are in
+ * a fixed order, so repeated calls give identical results.  T = 0 is a
+ * successful no-op.  Errors as moe_route. */
 int moe_load_balance(const moe_layer_t *L, const void *x, int64_t T, float *lb, float *mean_prob,
                      int32_t *counts, void *ws, size_t ws_bytes, void *stream);
 
