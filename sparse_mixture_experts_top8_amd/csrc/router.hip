@@ -14,13 +14,15 @@
 // denominator cancels); the kernel computes the latter.
 //
 // Two kernels.  router_logits_kernel: one workgroup per (64-token tile, or
-// 32-token tile for small batches, slice of H); the shared gate row rides along as column E, so the E + 1 columns
-// are 17 MFMA column blocks of 16.  Each wave streams its column blocks' rows
-// and the tile's x rows through a two-step register pipeline of 64-wide
-// k-steps (each row's whole 128-byte line per step) and writes fp32 partial
-// sums (one fp32 accumulator chain of at most H / 32 MFMAs per slice).  For large batches the router is read once per 64 tokens: its
-// re-reads through L2, not the arithmetic, set the kernel's pace.  Small batches split H into up
-// to H/64 slices so that the launch still spans the chip.
+// 32-token tile for small batches, slice of H); the shared gate row rides
+// along as column E, so the E + 1 columns are 17 MFMA column blocks of 16.
+// Each wave streams its column blocks' rows and the tile's x rows through a
+// two-step register pipeline of 64-wide k-steps (each row's whole 128-byte
+// line per step) and writes fp32 partial sums (one fp32 accumulator chain of
+// at most H / 32 MFMAs per slice).  For large batches the router is read
+// once per 64 tokens: its re-reads through L2, not the arithmetic, set the
+// kernel's pace.  Small batches split H into up to H/64 slices so that the
+// launch still spans the chip.
 // router_select_kernel (for the load-balance statistic, which needs its
 // per-block probability sums): one workgroup of 16 waves per 32 tokens sums
 // the slices in a fixed order and selects, two tokens per wave, and writes
