@@ -14,7 +14,8 @@
 // denominator cancels); the kernel computes the latter.
 //
 // Two kernels.  router_logits_kernel: one workgroup per (64-token tile, or
-// 32-token tile for small batches, slice of H); the shared gate row rides
+// 32-token tile for small batches and 128-token tile for large ones, slice of
+// H); the shared gate row rides
 // along as column E, so the E + 1 columns are 17 MFMA column blocks of 16.
 // Each wave streams its column blocks' rows and the tile's x rows through a
 // two-step register pipeline of 64-wide k-steps (each row's whole 128-byte
@@ -37,6 +38,9 @@ namespace {
 
 constexpr int kTok = kRouterTokens;      // 32 tokens per select block
 constexpr int kSmallT = 256;             // up to this many tokens: 32-token logits tiles, else 64
+constexpr int kLargeT = 8192;            // from this many tokens: 128-token logits tiles (the router is
+                                         // read half as often; zipf16384 router 90 -> 80 us, while at
+                                         // 4096 tokens the extra H slices cost more than that saves)
 constexpr int kColBlocks = 5;            // column blocks per wave (17 for E = 256, plus the gate column)
 constexpr int kDepth = 2;                // 64-wide k-steps in flight per wave
 constexpr int kMaxRouterCols = 260;      // router_cols(256)
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(1024) void load_balance_kernel(LayerArgs L, int T, 
 
 }  // namespace
 
-static int logits_tile(int T) { return T <= kSmallT ? 32 : 64; }
+static int logits_tile(int T) { return T <= kSmallT ? 32 : (T >= kLargeT ? 128 : 64); }
 
 int router_ksplit(int T, int H) {
   const int ntiles = (T + logits_tile(T) - 1) / logits_tile(T);
@@ -404,8 +408,10 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
   const int hn = router_blocks(T) * L.E;
   if (tile == 32)
     hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn);
-  else
+  else if (tile == 64)
     hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn);
+  else
+    hipLaunchKernelGGL(router_logits_kernel<8>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (per_token)

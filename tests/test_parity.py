@@ -132,9 +132,9 @@ def toy():
 # 2048 / 2049: the last batch dispatched by one workgroup and the first by the
 # multi-launch dispatch (router block histograms); 6000: ~1500 slots per toy
 # expert, more than eight 160-row tiles, so the groups' tiles are listed in
-# blocks of eight row tiles.
+# blocks of eight row tiles; 9000: 128-token router tiles.
 @pytest.mark.parametrize("T", [8, 1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 129, 300, 1000, 2048, 2049,
-                               6000])
+                               6000, 9000])
 def test_toy_parity(toy, T):
     d, bits, layer = toy
     _say(f"case toy T={T}")
