@@ -58,15 +58,16 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
   __shared__ int wave_tot[4];
   const int e = threadIdx.x;
   const int E = L.E, K = L.K;
+  const int bm = gemm_bm(T, K, E);
   const int cnt = e < E ? w.offsets[e] : 0;
   const int incl = block_inclusive_scan(cnt, wave_tot);
   if (e < E) w.offsets[e] = incl - cnt;
   if (e == 0) w.offsets[E] = T * K;
 
-  // Tiles per group: ceil(rows / BM) row tiles x (weight rows / BNW) column tiles.
+  // Tiles per group: ceil(rows / bm) row tiles x (weight rows / BNW) column tiles.
   int gu = 0, dn = 0;
   if (e < E) {
-    int mt = (cnt + kGemmBM - 1) / kGemmBM;
+    int mt = (cnt + bm - 1) / bm;
     gu = mt * ((2 * L.I + kGemmBNW - 1) / kGemmBNW);
     dn = mt * (L.H / kGemmBNW);
   }
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
     w.tiles_dn[e] = dn_incl - dn;
   }
   if (e == E - 1) {
-    const int mt = (T + kGemmBM - 1) / kGemmBM;
+    const int mt = (T + bm - 1) / bm;
     w.tiles_gu[E] = gu_incl;
     w.tiles_dn[E] = dn_incl;
     w.tiles_gu[E + 1] = gu_incl + mt * ((2 * L.Is + kGemmBNW - 1) / kGemmBNW);
@@ -89,10 +90,11 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
 // its tiles in both grouped GEMMs, in gemm_tile_order.
 __device__ void dispatch_tiles(LayerArgs L, int T, const Work& w, int g) {
   const int E = L.E;
+  const int bm = gemm_bm(T, L.K, E);
   const bool shared = g == E;
   const int seg0 = shared ? 0 : w.offsets[g];
   const int nrows = shared ? T : w.offsets[g + 1] - seg0;
-  const int mt = (nrows + kGemmBM - 1) / kGemmBM;
+  const int mt = (nrows + bm - 1) / bm;
   const int ngu = (2 * (shared ? L.Is : L.I) + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
   const int bgu = w.tiles_gu[g], bdn = w.tiles_dn[g];
   for (int i = threadIdx.x; i < mt * ngu; i += 256) {
@@ -152,6 +154,7 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
   __shared__ int wave_tot[kSmallThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = L.E, K = L.K, TK = T * K;
+  const int bm = gemm_bm(T, K, E);
   const int nblk = router_blocks(T);
   for (int i = tid; i < nblk * E; i += kSmallThreads) s_mask[i] = 0u;
   __syncthreads();
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
       const int cnt = e < E ? s_cnt[e] : 0;
-      const int mt = (cnt + kGemmBM - 1) / kGemmBM;
+      const int mt = (cnt + bm - 1) / bm;
       v[j] = wave == 0 ? cnt : (wave == 1 ? mt * ((2 * L.I + kGemmBNW - 1) / kGemmBNW) : mt * (L.H / kGemmBNW));
       run += v[j];
     }
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
       ex += v[j];
     }
     if (lane == 63) {
-      const int mt = (T + kGemmBM - 1) / kGemmBM;
+      const int mt = (T + bm - 1) / bm;
       dst[E] = incl;
       if (wave == 1) dst[E + 1] = incl + mt * ((2 * L.Is + kGemmBNW - 1) / kGemmBNW);
       if (wave == 2) dst[E + 1] = incl + mt * (L.H / kGemmBNW);
@@ -209,24 +212,30 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
     w.tiles_gu[g] = s_tgu[g];
     w.tiles_dn[g] = s_tdn[g];
   }
-  // Tile descriptors, one thread per group (gemm_tile_order).
-  if (tid <= E) {
-    const int g = tid;
-    const bool shared = g == E;
-    const int seg0 = shared ? 0 : s_off[g];
-    const int nrows = shared ? T : s_cnt[g];
-    const int mt = (nrows + kGemmBM - 1) / kGemmBM;
-    const int ngu = (2 * (shared ? L.Is : L.I) + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
-    // gemm_tile_order as nested loops (one thread writes all of a group's
-    // descriptors: no divisions on that serial path).
-    int4* gu = w.tdesc_gu + s_tgu[g];
-    int4* dn = w.tdesc_dn + s_tdn[g];
-    for (int b0 = 0; b0 < mt; b0 += kGemmRowBlock) {
-      const int rows = min(kGemmRowBlock, mt - b0);
-      for (int nt = 0; nt < ngu; ++nt)
-        for (int r = 0; r < rows; ++r) *gu++ = make_int4(g, seg0, nrows, (b0 + r) | (nt << 16));
-      for (int nt = 0; nt < ndn; ++nt)
-        for (int r = 0; r < rows; ++r) *dn++ = make_int4(g, seg0, nrows, (b0 + r) | (nt << 16));
+  // Tile descriptors in gemm_tile_order, one item per (group, column tile)
+  // of either GEMM, waves over column tiles and lanes over groups.  Item
+  // (g, nt) writes column tile nt of every row block of group g: a block of
+  // `rows` row tiles starts at b0 * ncol and holds that column tile at
+  // nt * rows + row.  (Small batches give the shared group many row tiles,
+  // so one thread per group would be a long serial path.)
+  {
+    const int ngu_r = (2 * L.I + kGemmBNW - 1) / kGemmBNW, ngu_s = (2 * L.Is + kGemmBNW - 1) / kGemmBNW;
+    const int ndn = L.H / kGemmBNW, gumax = max(ngu_r, ngu_s), ncols = gumax + ndn;
+    for (int c = wave; c < ncols; c += kSmallThreads / 64) {
+      for (int g = lane; g <= E; g += 64) {
+        const bool shared = g == E, gu = c < gumax;
+        const int ncol = gu ? (shared ? ngu_s : ngu_r) : ndn, nt = gu ? c : c - gumax;
+        if (nt >= ncol) continue;
+        const int seg0 = shared ? 0 : s_off[g];
+        const int nrows = shared ? T : s_cnt[g];
+        const int mt = (nrows + bm - 1) / bm;
+        int4* base = gu ? w.tdesc_gu + s_tgu[g] : w.tdesc_dn + s_tdn[g];
+        for (int b0 = 0; b0 < mt; b0 += kGemmRowBlock) {
+          const int rows = min(kGemmRowBlock, mt - b0);
+          int4* d = base + b0 * ncol + nt * rows;
+          for (int r = 0; r < rows; ++r) d[r] = make_int4(g, seg0, nrows, (b0 + r) | (nt << 16));
+        }
+      }
     }
   }
   // Scatter.

@@ -15,11 +15,12 @@
 // One workgroup per tile of 160 rows x 128 weight rows (160 rows hold a
 // typical expert of a 4096-token batch, about 128 +- 11 rows, in one tile, so
 // its weights stream once); two workgroups share a CU, so one's start-up
-// overlaps the other's streaming.  Wave w owns weight
+// overlaps the other's streaming.  Batches of a few rows per expert use
+// 32-row tiles, four workgroups per CU.  Wave w owns weight
 // rows 32w .. 32w + 31 of the tile as two 16-column MFMA blocks: for gate_up
 // the gate rows and the up rows of the same 16 inner rows (SiLU(g) * u is
 // formed in registers, both blocks having the same layout), for down 32 output
-// columns.  Each wave covers all 160 rows.
+// columns.  Each wave covers all rows of the tile.
 //
 // k advances in steps of 64 through a four-deep ring, three steps in flight:
 // the weight fragments of a wave are needed by that wave alone and go straight
@@ -53,15 +54,21 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM;      // 160 rows
 constexpr int BN = kGemmBNW;     // 128 weight rows
 constexpr int BK = 64;
 constexpr int NS = 4;            // ring depth (activation LDS stages = weight register slots)
-constexpr int kATile = BM * BK * 2;     // 20 KB
-constexpr int kMBlocks = BM / 16;       // 16-row MFMA blocks
-constexpr int kADma = BM * 8 / 256;     // direct-to-LDS instructions per wave per step (16-byte units / 256 threads)
-constexpr int kVmPerStep = kADma + 4;   // per wave: activation loads + 4 weight loads
-static_assert(kMBlocks == 10 && (BM * 8) % 256 == 0, "the step reads the tile rows in two groups of five blocks");
+// Shape of a tile of BM rows (160, or 32 for small batches).
+template <int BM>
+struct TileShape {
+  static constexpr int kATile = BM * BK * 2;        // activation stage: 20 KB (160 rows), 4 KB (32 rows)
+  static constexpr int kMBlocks = BM / 16;          // 16-row MFMA blocks
+  static constexpr int kGroup = kMBlocks < 5 ? kMBlocks : 5;   // blocks read from LDS together
+  static constexpr int kADma = BM * 8 / 256;        // direct-to-LDS instructions per wave per step (16-byte units / 256 threads)
+  static constexpr int kVmPerStep = kADma + 4;      // per wave: activation loads + 4 weight loads
+  static constexpr int kPerCU = BM > 64 ? 2 : 4;    // workgroups per CU (LDS: NS stages each)
+  static_assert((BM * 8) % 256 == 0 && (kMBlocks == kGroup || kMBlocks == 2 * kGroup),
+                "rows are read in one or two groups of blocks");
+};
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -79,14 +86,17 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
 // Operands of five consecutive 16-row blocks I0 .. I0 + 4: one base address
 // per lane, the blocks 2048 bytes apart (16 rows of 128 bytes; the chunk
 // swizzle depends on row % 8 only, which is the same in every block).
-template <int I0, int... I>
-__device__ __forceinline__ void lds_read_group(u32x4 (&a)[5], uint32_t addr, std::integer_sequence<int, I...>) {
+template <int I0, int G, int... I>
+__device__ __forceinline__ void lds_read_group(u32x4 (&a)[G], uint32_t addr, std::integer_sequence<int, I...>) {
   ((a[I] = lds_read16<2048 * (I0 + I)>(addr)), ...);
 }
 // Waits for the LDS reads and ties their result registers to the wait, so
 // that no use of them can be scheduled before it.
 __device__ __forceinline__ void wait_lds(u32x4 (&a)[5]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]) : : "memory");
+}
+__device__ __forceinline__ void wait_lds(u32x4 (&a)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]) : : "memory");
 }
 // s_waitcnt vmcnt(N) through the builtin, which the compiler's own wait
 // insertion takes into account (it cannot see inside inline asm, and would
@@ -112,14 +122,18 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // WAUX: cache policy of the weight loads (0, or kNonTemporal for batches so
-// small that each weight fragment feeds one tile of a few rows).
-template <bool GATE_UP, int WAUX>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
+// small that each weight fragment feeds one tile of a few rows).  BM: rows
+// per tile.
+template <bool GATE_UP, int WAUX, int BM>
+__global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
                                                              Work w, const int* __restrict__ prefix,
                                                              const int4* __restrict__ tdesc,
                                                              const int* __restrict__ slot_tok,
                                                              const int* __restrict__ window,
                                                              const int* __restrict__ slot_map) {
+  using S = TileShape<BM>;
+  constexpr int kATile = S::kATile, kMBlocks = S::kMBlocks, kGroup = S::kGroup, kADma = S::kADma;
+  constexpr int kVmPerStep = S::kVmPerStep;
   __shared__ __attribute__((aligned(1024))) char lds[NS * kATile];
 
   const int E = L.E, K = L.K, H = L.H;
@@ -257,23 +271,25 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t sa = lds_base + st * kATile + l16 * 128 + (((2 * q + h) ^ (l16 & 7)) << 4);
-      u32x4 av[5];
-      lds_read_group<0>(av, sa, std::make_integer_sequence<int, 5>{});
+      u32x4 av[kGroup];
+      lds_read_group<0>(av, sa, std::make_integer_sequence<int, kGroup>{});
       wait_lds(av);
 #pragma unroll
-      for (int i = 0; i < 5; ++i) {
+      for (int i = 0; i < kGroup; ++i) {
         acc[i][0] = mfma16(av[i], wcur[0][h], acc[i][0]);
         acc[i][1] = mfma16(av[i], wcur[1][h], acc[i][1]);
       }
-      // The second group of five 16-row blocks is skipped when the tile's rows
-      // end before it (uniform branch).
-      if (mblocks > 5) {
-        lds_read_group<5>(av, sa, std::make_integer_sequence<int, 5>{});
-        wait_lds(av);
+      // A second group of 16-row blocks (160-row tiles) is skipped when the
+      // tile's rows end before it (uniform branch).
+      if constexpr (kMBlocks > kGroup) {
+        if (mblocks > kGroup) {
+          lds_read_group<kGroup>(av, sa, std::make_integer_sequence<int, kGroup>{});
+          wait_lds(av);
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          acc[5 + i][0] = mfma16(av[i], wcur[0][h], acc[5 + i][0]);
-          acc[5 + i][1] = mfma16(av[i], wcur[1][h], acc[5 + i][1]);
+          for (int i = 0; i < kGroup; ++i) {
+            acc[kGroup + i][0] = mfma16(av[i], wcur[0][h], acc[kGroup + i][0]);
+            acc[kGroup + i][1] = mfma16(av[i], wcur[1][h], acc[kGroup + i][1]);
+          }
         }
       }
     }
@@ -306,7 +322,8 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(LayerArgs L, const
   // stores 16-byte row chunks; rows past the group fall outside the store
   // resource and are dropped.
   barrier();
-  bf16_t* ep = reinterpret_cast<bf16_t*>(lds + wv * (BM * 32 * 2));    // 160 rows x 32 columns (10 KB) per wave
+  bf16_t* ep = reinterpret_cast<bf16_t*>(lds + wv * (BM * 32 * 2));    // BM rows x 32 columns per wave
+  static_assert(4 * BM * 32 * 2 <= NS * kATile, "the epilogue tiles fit in the ring");
   constexpr int kCols = GATE_UP ? 16 : 32;
 #pragma unroll
   for (int i = 0; i < kMBlocks; ++i)
@@ -409,13 +426,22 @@ unsigned gemm_grid(int64_t bound) { return (unsigned)(8 * ((bound + 7) / 8)); }
 // zipf16384 +19 %, where hot experts' weights are reused across row tiles).
 static bool stream_weights(const LayerArgs& L, int T) { return (int64_t)T * L.K <= 16 * (int64_t)L.E; }
 
+// Kernel of a batch: 32-row tiles for the smallest batches (gemm_bm), weight
+// cache policy by stream_weights.
+template <bool GATE_UP>
+static auto gemm_kernel_for(const LayerArgs& L, int T) {
+  if (gemm_small_rows(T, L.K, L.E)) return grouped_gemm_kernel<GATE_UP, kNonTemporal, kGemmBMSmall>;
+  return stream_weights(L, T) ? grouped_gemm_kernel<GATE_UP, kNonTemporal, kGemmBM>
+                              : grouped_gemm_kernel<GATE_UP, 0, kGemmBM>;
+}
+
 hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work& w, int num_cus,
                           hipStream_t s, const int* window, const int* slot_map) {
   (void)num_cus;
   // The dispatch tables go in as separate read-only arguments: uniform reads of
   // them then compile to scalar loads.
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, 2 * L.I, 2 * L.Is);
-  auto k = stream_weights(L, T) ? grouped_gemm_kernel<true, kNonTemporal> : grouped_gemm_kernel<true, 0>;
+  auto k = gemm_kernel_for<true>(L, T);
   hipLaunchKernelGGL(k, dim3(gemm_grid(bound)), dim3(256), 0, s, L, x, T, w, (const int*)w.tiles_gu,
                      (const int4*)w.tdesc_gu, (const int*)w.slot_tok, window, slot_map);
   return hipGetLastError();
@@ -425,7 +451,7 @@ hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hi
                        const int* slot_map) {
   (void)num_cus;
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, L.H, L.H);
-  auto k = stream_weights(L, T) ? grouped_gemm_kernel<false, kNonTemporal> : grouped_gemm_kernel<false, 0>;
+  auto k = gemm_kernel_for<false>(L, T);
   hipLaunchKernelGGL(k, dim3(gemm_grid(bound)), dim3(256), 0, s, L, (const bf16_t*)nullptr, T, w,
                      (const int*)w.tiles_dn, (const int4*)w.tdesc_dn, (const int*)w.slot_tok, window, slot_map);
   return hipGetLastError();

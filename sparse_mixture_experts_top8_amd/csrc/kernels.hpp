@@ -8,14 +8,26 @@ namespace moe {
 
 // Router tile: tokens per router workgroup (also the dispatch block size).
 constexpr int kRouterTokens = 32;
-// Grouped-GEMM tile: rows (slots) per tile, weight rows per tile.
+// Grouped-GEMM tile: rows (slots) per tile, weight rows per tile.  Batches
+// of at most 8 slots per expert on average (T K <= 8 E) use 32-row tiles:
+// their groups are a few rows each, and the smaller tile leaves LDS for four
+// workgroups per CU instead of two, which hides the start of the short down
+// tiles (MI355X: 64 tokens 257 -> 252 us, 128 tokens 285 -> 281 us; at 384
+// and 512 tokens, 16-row tiles of the shared expert's rows cost more than
+// that saves: 313 -> 320 and 326 -> 330 us).
 constexpr int kGemmBM = 160;
+constexpr int kGemmBMSmall = 32;
 constexpr int kGemmBNW = 128;   // weight rows per tile: gate_up 64 gate + 64 up; down 128 H cols
+__host__ __device__ inline bool gemm_small_rows(int64_t T, int K, int E) { return T * K <= 8 * (int64_t)E; }
+__host__ __device__ inline int gemm_bm(int64_t T, int K, int E) {
+  return gemm_small_rows(T, K, E) ? kGemmBMSmall : kGemmBM;
+}
 // Upper bound of the tiles of one grouped GEMM (workspace and grid size):
 // every group adds at most one partial row tile.
 __host__ __device__ inline int64_t gemm_tile_bound(int64_t T, int K, int E, int wrows, int wrows_shared) {
   const int64_t nt = (wrows + kGemmBNW - 1) / kGemmBNW, nts = (wrows_shared + kGemmBNW - 1) / kGemmBNW;
-  return ((T * K + kGemmBM - 1) / kGemmBM + E) * nt + ((T + kGemmBM - 1) / kGemmBM) * nts;
+  const int bm = gemm_bm(T, K, E);
+  return ((T * K + bm - 1) / bm + E) * nt + ((T + bm - 1) / bm) * nts;
 }
 
 // Order of a group's mt x nct tiles in the dispatch list: blocks of
