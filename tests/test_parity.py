@@ -785,6 +785,26 @@ def test_toy_tiled_matches_row_major(toy, T):
         assert torch.equal(st.view(torch.int16), got.view(torch.int16))
 
 
+def test_full_gemm_tile_regimes(full):
+    # Both sides of each switch of the grouped GEMMs at full shape: 32-row
+    # tiles up to 8 slots per expert on average (256 tokens), 160-row tiles
+    # with streamed weight loads up to 16 (512 tokens), then plain loads.
+    # Every row against the oracle, and the tiled expert layout bitwise equal
+    # to the row-major one.
+    moe = _moe()
+    d, bits, layer, _, _ = full
+    t = layer.tiled()
+    for T in (256, 257, 512, 513):
+        _say(f"case full GEMM tile regime T={T}")
+        xb = mi.make_x(d, T, 9700 + T)
+        r, out = run_layer(layer, xb, want_logits=True)
+        gi = check_routing(xb, bits, d, r, f"tile regime T={T}")
+        check_output(xb, bits, d, gi, _np(out.float()), np.arange(T), f"tile regime T={T}")
+        got = moe.forward(moe.bits_to_device(xb, "cuda"), t)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), out.view(torch.int16)), f"T={T}"
+
+
 def test_full_tiled_matches_row_major(full):
     moe = _moe()
     d, bits, layer, _, _ = full
