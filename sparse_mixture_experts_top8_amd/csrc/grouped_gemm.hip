@@ -363,10 +363,11 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
 // order, fp32 sum.  The K + 1 row indices and scales are requested first,
 // then all K + 1 rows, so the loads overlap instead of forming a chain.
 constexpr int kMaxK = 8;
-__global__ __launch_bounds__(256) void combine_kernel(int T, int H, int K, Work w, bf16_t* __restrict__ out,
+template <int NT>
+__global__ __launch_bounds__(NT) void combine_kernel(int T, int H, int K, Work w, bf16_t* __restrict__ out,
                                                       const bf16_t* __restrict__ residual) {
   const int per_tok = H >> 3;
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t idx = (size_t)blockIdx.x * NT + threadIdx.x;
   if (idx >= (size_t)T * per_tok) return;
   const int t = (int)(idx / per_tok), c = (int)(idx % per_tok) * 8;
   size_t row[kMaxK + 1];
@@ -460,7 +461,14 @@ hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hi
 hipError_t launch_combine(const LayerArgs& L, int T, const Work& w, bf16_t* out, hipStream_t s,
                           const bf16_t* residual) {
   const size_t n = (size_t)T * (L.H / 8);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, L.H, L.K, w, out,
+  // Under 256 workgroups of 256 threads, 64-thread workgroups spread the
+  // rows over more CUs (decode64 combine 6.7 -> 6.3 us).
+  if (n < 256 * 256) {
+    hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, s, T, L.H, L.K, w, out,
+                       residual);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(combine_kernel<256>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T, L.H, L.K, w, out,
                      residual);
   return hipGetLastError();
 }
