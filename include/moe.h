@@ -95,7 +95,9 @@ typedef struct moe_layer {
 } moe_layer_t;
 
 /* Bytes of device workspace that moe_route / moe_forward need for T tokens
- * (0 for T <= 0 or unsupported dimensions).  Host-only; no HIP call. */
+ * (0 for T <= 0 or unsupported dimensions).  Non-decreasing in T: a workspace
+ * of moe_workspace_bytes(L, T) bytes serves every call of 1..T tokens.
+ * Host-only; no HIP call. */
 size_t moe_workspace_bytes(const moe_layer_t *L, int64_t T);
 
 /* Check the arguments of a moe_forward call without touching the GPU.

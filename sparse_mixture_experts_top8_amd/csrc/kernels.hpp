@@ -23,11 +23,19 @@ __host__ __device__ inline int gemm_bm(int64_t T, int K, int E) {
   return gemm_small_rows(T, K, E) ? kGemmBMSmall : kGemmBM;
 }
 // Upper bound of the tiles of one grouped GEMM (workspace and grid size):
-// every group adds at most one partial row tile.
-__host__ __device__ inline int64_t gemm_tile_bound(int64_t T, int K, int E, int wrows, int wrows_shared) {
+// every group adds at most one partial row tile.  Past the switch to 160-row
+// tiles the bound keeps the 32-row bound of the largest small batch, so it
+// never decreases as T grows (a workspace sized for T serves smaller batches).
+__host__ __device__ inline int64_t gemm_tile_bound_bm(int64_t T, int K, int E, int wrows, int wrows_shared, int bm) {
   const int64_t nt = (wrows + kGemmBNW - 1) / kGemmBNW, nts = (wrows_shared + kGemmBNW - 1) / kGemmBNW;
-  const int bm = gemm_bm(T, K, E);
   return ((T * K + bm - 1) / bm + E) * nt + ((T + bm - 1) / bm) * nts;
+}
+__host__ __device__ inline int64_t gemm_tile_bound(int64_t T, int K, int E, int wrows, int wrows_shared) {
+  if (gemm_small_rows(T, K, E)) return gemm_tile_bound_bm(T, K, E, wrows, wrows_shared, kGemmBMSmall);
+  const int64_t small_max = 8 * (int64_t)E / K;   // largest batch with 32-row tiles
+  const int64_t a = gemm_tile_bound_bm(small_max, K, E, wrows, wrows_shared, kGemmBMSmall);
+  const int64_t b = gemm_tile_bound_bm(T, K, E, wrows, wrows_shared, kGemmBM);
+  return a > b ? a : b;
 }
 
 // Order of a group's mt x nct tiles in the dispatch list: blocks of
@@ -63,6 +71,8 @@ __host__ __device__ inline bool dispatch_single_block(int64_t T) { return router
 __host__ __device__ inline int router_cols(int E) { return (E + 1 + 3) & ~3; }
 // Slices of H the router's logits GEMM is split into for T tokens.
 int router_ksplit(int T, int H);
+// Upper bound of ksplit(T') * T' over T' <= T (rows of router partial sums).
+int64_t router_partial_rows(int64_t T, int H);
 
 // Fused decode path (T <= kDecodeMaxT, H <= 2048, I <= 512, Is <= 512, and the
 // per-workgroup row shares of decode_fits).

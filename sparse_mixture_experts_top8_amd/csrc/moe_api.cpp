@@ -75,7 +75,7 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   c.w.topk_idx = (int32_t*)take(tk * 4);
   c.w.topk_w = (float*)take(tk * 4);
   c.w.gate_s = (float*)take(t * 4);
-  c.w.rlog = (float*)take((size_t)moe::router_ksplit((int)T, (int)H) * t * moe::router_cols((int)E) * 4);
+  c.w.rlog = (float*)take((size_t)moe::router_partial_rows(T, (int)H) * moe::router_cols((int)E) * 4);
   c.w.blk_counts = (int32_t*)take(nblk * E * 4);
   c.w.offsets = (int32_t*)take((E + 1) * 4);
   c.w.tiles_gu = (int32_t*)take((E + 2) * 4);
@@ -142,9 +142,14 @@ DecodeCarve carve_decode(const moe_layer_t* L, int64_t T, char* base) {
   return c;
 }
 
+// Non-decreasing in T, so that a workspace sized for T serves every call of
+// 1..T tokens: every region of carve() grows with T (the router partials and
+// tile descriptors through their bounds), and past the fused decode path's
+// largest batch its workspace for that batch is still covered.
 size_t workspace_need(const moe_layer_t* L, int64_t T) {
   const size_t grouped = carve(L, T, nullptr).bytes;
-  return decode_shape(L, T) ? std::max(grouped, carve_decode(L, T, nullptr).bytes) : grouped;
+  const int64_t td = std::min<int64_t>(T, moe::kDecodeMaxT);
+  return decode_shape(L, td) ? std::max(grouped, carve_decode(L, td, nullptr).bytes) : grouped;
 }
 
 // Call-unique epochs for the decode path's start protocol: a per-process

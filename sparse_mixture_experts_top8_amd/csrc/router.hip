@@ -396,6 +396,16 @@ int router_ksplit(int T, int H) {
   return s;
 }
 
+// Rows of partial sums the logits kernel writes is ksplit(T) * T.  Upper
+// bound over every batch of at most T tokens (workspace sizing, which must
+// not shrink as T grows): ksplit <= min(16, H / 64), and when ksplit >= 2 it
+// was doubled from a value whose product with the tile count was below 256,
+// so ksplit * T < 512 * tile(T); every term is non-decreasing in T.
+int64_t router_partial_rows(int64_t T, int H) {
+  const int64_t cap = std::min(16, H / 64);
+  return std::max<int64_t>(T, std::min<int64_t>(cap * T, 512 * (int64_t)logits_tile((int)T)));
+}
+
 hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work& w,
                          float* logits_out, hipStream_t s, float* psum_out) {
   const int ks = router_ksplit(T, L.H), tile = logits_tile(T);

@@ -55,6 +55,20 @@ def test_workspace_bytes():
     assert _lib.lib.moe_workspace_bytes(_layer(H=100), 4) == 0
 
 
+def test_workspace_bytes_never_decrease():
+    # A workspace sized for T serves every batch of 1..T tokens: the size is
+    # non-decreasing across every switch of the paths (fused decode at 16
+    # tokens, 32-row GEMM tiles, router tile sizes and H splits).
+    for dims in [(2048, 256, 8, 512, 512), (256, 16, 4, 64, 64), (2048, 256, 1, 512, 512),
+                 (2048, 64, 8, 512, 512), (256, 8, 8, 64, 64)]:
+        L = _layer(*dims)
+        prev = 0
+        for T in range(1, 20001):
+            b = _lib.lib.moe_workspace_bytes(L, T)
+            assert b >= prev, (dims, T, prev, b)
+            prev = b
+
+
 def _validate(L, x=FAKE, T=4, out=FAKE, ws=FAKE, nbytes=None):
     if nbytes is None:
         nbytes = _lib.lib.moe_workspace_bytes(L, max(T, 1))

@@ -805,6 +805,25 @@ def test_full_gemm_tile_regimes(full):
         assert torch.equal(got.view(torch.int16), out.view(torch.int16)), f"T={T}"
 
 
+def test_full_workspace_sized_for_largest_batch(full):
+    # One workspace sized for 600 tokens serves batches of every path below
+    # it (fused decode, 32-row and 160-row GEMM tiles) with the same bits as
+    # a workspace of each batch's own size.
+    moe = _moe()
+    d, bits, layer, _, _ = full
+    big = layer.workspace(600)
+    for T in (1, 16, 17, 256, 257, 600):
+        _say(f"case full shared workspace T={T}")
+        x = moe.bits_to_device(mi.make_x(d, T, 9600 + T), "cuda")
+        a = moe.forward(x, layer, ws=big)
+        torch.cuda.synchronize()
+        if T <= 16:
+            assert decode_error_word(big) == 0, "decode path wait timed out"
+        b = moe.forward(x, layer)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"T={T}"
+
+
 def test_full_tiled_matches_row_major(full):
     moe = _moe()
     d, bits, layer, _, _ = full
