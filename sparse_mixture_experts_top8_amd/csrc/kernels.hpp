@@ -13,8 +13,8 @@ constexpr int kRouterTokens = 32;
 // their groups are a few rows each, and the smaller tile leaves LDS for four
 // workgroups per CU instead of two, which hides the start of the short down
 // tiles (MI355X: 64 tokens 257 -> 252 us, 128 tokens 285 -> 281 us; at 384
-// and 512 tokens, 16-row tiles of the shared expert's rows cost more than
-// that saves: 313 -> 320 and 326 -> 330 us).
+// and 512 tokens the shared expert's 12-16 row tiles, each re-reading its
+// weights, cost more than that saves: 313 -> 320 and 326 -> 330 us).
 constexpr int kGemmBM = 160;
 constexpr int kGemmBMSmall = 32;
 constexpr int kGemmBNW = 128;   // weight rows per tile: gate_up 64 gate + 64 up; down 128 H cols
