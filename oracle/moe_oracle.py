@@ -47,7 +47,8 @@ notes of this repository):
   h / sqrt(mean(h^2) + eps) * w.
 
 Inputs are bf16 bit patterns (uint16 arrays); parameters are passed as a
-mapping keyed by the model page's member names: ``gate.weight``,
+mapping of bf16 bit patterns, or of their float64 values decoded once with
+``decode_params``, keyed by the model page's member names: ``gate.weight``,
 ``gate_up_proj``, ``down_proj``, ``shared_expert.gate.weight``,
 ``shared_expert.up.weight``, ``shared_expert.down.weight``,
 ``shared_expert_gate.weight``.
@@ -74,6 +75,19 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def param_values(a: np.ndarray) -> np.ndarray:
+    """Values of a parameter: bf16 bit patterns (uint16) are decoded exactly;
+    an array of float64 values (``decode_params``) is taken as it is."""
+    a = np.asarray(a)
+    return a if a.dtype == np.float64 else bf16_to_f64(a)
+
+
+def decode_params(params: dict) -> dict:
+    """Every parameter decoded once to float64 (the same values the functions
+    below decode on each use), so that repeated calls skip the decoding."""
+    return {name: bf16_to_f64(v) for name, v in params.items()}
+
+
 def round_bf16(v: np.ndarray) -> np.ndarray:
     """Nearest bfloat16 value of each float64, ties to the even significand.
 
@@ -91,6 +105,17 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     r = np.round(v / step) * step
     r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)
     return np.where(a == 0, v, r)
+
+
+def bf16_bits(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of values that are bf16 numbers already (for example
+    the output of ``round_bf16``): the value is exact in float32, whose top
+    half is its bf16 pattern.  Raises if a value is not a bf16 number."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32)
+    if np.any(u & np.uint32(0xFFFF)) or np.any(f.astype(np.float64) != np.asarray(v, dtype=np.float64)):
+        raise ValueError("not a bf16 value")
+    return (u >> np.uint32(16)).astype(np.uint16)
 
 
 # ---------------------------------------------------------------------------
@@ -114,7 +139,7 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 def router_logits(x: np.ndarray, router_w: np.ndarray) -> np.ndarray:
     """logits[t, e] = sum_h x[t, h] * W_r[e, h], float64 ([T, H] x [E, H] -> [T, E])."""
-    return bf16_to_f64(x) @ bf16_to_f64(router_w).T
+    return bf16_to_f64(x) @ param_values(router_w).T
 
 
 def softmax_rows(logits: np.ndarray) -> np.ndarray:
@@ -202,7 +227,7 @@ def route(x: np.ndarray, params: dict, K: int, logits_bf16: bool = False) -> dic
 def shared_gate(x: np.ndarray, params: dict, logits_bf16: bool = False) -> np.ndarray:
     """s[t] = sigmoid(x[t] . w_sg) for the [1, H] shared_expert_gate Linear
     (its output rounded to bf16 first with ``logits_bf16``)."""
-    z = (bf16_to_f64(x) @ bf16_to_f64(params["shared_expert_gate.weight"]).T)[:, 0]
+    z = (bf16_to_f64(x) @ param_values(params["shared_expert_gate.weight"]).T)[:, 0]
     return sigmoid(round_bf16(z) if logits_bf16 else z)
 
 
@@ -241,15 +266,15 @@ def swiglu(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarr
 
 def routed_expert(X: np.ndarray, params: dict, e: int, I: int) -> np.ndarray:
     """expert_e applied to float64 rows X: gate = gate_up_proj[e, :I], up = gate_up_proj[e, I:]."""
-    gu = bf16_to_f64(params["gate_up_proj"][e])
-    wd = bf16_to_f64(params["down_proj"][e])
+    gu = param_values(params["gate_up_proj"][e])
+    wd = param_values(params["down_proj"][e])
     return swiglu(X, gu[:I], gu[I:], wd)
 
 
 def shared_expert(X: np.ndarray, params: dict) -> np.ndarray:
-    return swiglu(X, bf16_to_f64(params["shared_expert.gate.weight"]),
-                  bf16_to_f64(params["shared_expert.up.weight"]),
-                  bf16_to_f64(params["shared_expert.down.weight"]))
+    return swiglu(X, param_values(params["shared_expert.gate.weight"]),
+                  param_values(params["shared_expert.up.weight"]),
+                  param_values(params["shared_expert.down.weight"]))
 
 
 def _dims(params: dict):
@@ -360,6 +385,15 @@ def rmsnorm(h: np.ndarray, norm_w: np.ndarray, eps: float) -> np.ndarray:
     H = bf16_to_f64(h)
     w = bf16_to_f64(norm_w).reshape(-1)
     return H / np.sqrt(np.mean(H * H, axis=1, keepdims=True) + eps) * w[None, :]
+
+
+def block_forward(h: np.ndarray, norm_w: np.ndarray, eps: float, params: dict, K: int,
+                  logits_bf16: bool = False):
+    """The MoE sub-block end to end: x = bf16(RMSNorm(h)), routed by the
+    oracle's own router, out = h + MoE(x).  Returns (out [T, H] float64,
+    x as bf16 bits [T, H])."""
+    x_bits = bf16_bits(round_bf16(rmsnorm(h, norm_w, eps)))
+    return bf16_to_f64(h) + forward(x_bits, params, K, logits_bf16), x_bits
 
 
 def block_forward_with_routing(h: np.ndarray, x_bits: np.ndarray, params: dict,

@@ -498,6 +498,61 @@ def test_block_forward_reduces_to_residual_and_layer():
     assert np.array_equal(O.block_forward_with_routing(h, x, z, idx), O.bf16_to_f64(h))
 
 
+def test_decoded_params_give_identical_results():
+    # Parameters decoded once (the CPU baseline's timing setup) are the same
+    # values: every result is bit-identical to decoding on each use.
+    d = mi.TOY
+    layer = _random_layer(d, 346)
+    dec = O.decode_params(layer)
+    assert all(v.dtype == np.float64 for v in dec.values())
+    x = mi.make_x(d, 11, 347)
+    assert np.array_equal(O.forward(x, dec, d.K), O.forward(x, layer, d.K))
+    assert np.array_equal(O.forward_dense(x, dec, d.K), O.forward_dense(x, layer, d.K))
+    for mode in (False, True):
+        a, b = O.route(x, dec, d.K, mode), O.route(x, layer, d.K, mode)
+        assert all(np.array_equal(a[k], b[k]) for k in a)
+
+
+def test_bf16_bits_is_the_exact_encoding():
+    rng = np.random.default_rng(342)
+    # Every finite bf16 pattern round-trips through its value.
+    b = rng.integers(0, 1 << 16, 20000, dtype=np.uint32).astype(np.uint16)
+    b = b[(b & 0x7F80) != 0x7F80]
+    assert np.array_equal(O.bf16_bits(O.bf16_to_f64(b)), b)
+    # Rounded values encode as the IEEE float32 -> bf16 conversion of values
+    # float32 holds exactly (no double rounding in between).
+    v = rng.normal(0, 3, 5000).astype(np.float32).astype(np.float64)
+    assert np.array_equal(O.bf16_bits(O.round_bf16(v)), mi.f32_to_bf16_bits(v.astype(np.float32)))
+    for bad in (1.0 + 2.0 ** -9, 0.1):
+        with pytest.raises(ValueError):
+            O.bf16_bits(np.array([bad]))
+
+
+def test_block_forward_chain_closed_form():
+    # Constant rows c with eps = 0: RMSNorm gives sign(c) * w exactly, a bf16
+    # value, so the chain must route and evaluate exactly those activations
+    # and add h.
+    d = mi.TOY
+    layer = _random_layer(d, 343)
+    rng = np.random.default_rng(344)
+    w = _bits(rng.normal(1.0, 0.2, d.H))
+    cs = np.array([0.75, -3.0, 2.0 ** -6, 1.5])
+    h = _bits(np.repeat(cs[:, None], d.H, axis=1))
+    out, x = O.block_forward(h, w, 0.0, layer, d.K)
+    want_x = _bits(np.sign(cs)[:, None] * O.bf16_to_f64(w)[None, :])
+    assert np.array_equal(x, want_x)
+    assert np.array_equal(out, O.bf16_to_f64(h) + O.forward(want_x, layer, d.K))
+    # Token permutation permutes the rows; h = 0 gives 0 (x = 0, layer of 0 = 0).
+    hr = mi.make_x(d, 9, 345)
+    o1, x1 = O.block_forward(hr, w, 1e-6, layer, d.K)
+    p = rng.permutation(9)
+    o2, x2 = O.block_forward(hr[p], w, 1e-6, layer, d.K)
+    assert np.array_equal(x2, x1[p])
+    np.testing.assert_allclose(o2, o1[p], rtol=1e-12, atol=1e-15)
+    oz, xz = O.block_forward(np.zeros((3, d.H), np.uint16), w, 1e-6, layer, d.K)
+    assert np.all(oz == 0.0) and np.all(O.bf16_to_f64(xz) == 0.0)
+
+
 # ---------------------------------------------------------------------------
 # bf16-logit routing mode: the model page types the gate projections' outputs
 # as T = bf16.  Rounding pinned against IEEE conversion and exact rationals;
