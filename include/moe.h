@@ -38,6 +38,12 @@
  *    moe_last_error() gives a per-thread text for the last failure.
  *  - Inputs are assumed finite; NaN/Inf in x or the weights give unspecified
  *    routing.
+ *  - Workspace: device memory of moe_workspace_bytes(L, T) bytes, 16-byte
+ *    aligned, owned by the caller.  A new workspace must be zero-filled once
+ *    before its first call (hipMemset, or allocate it zeroed); the library
+ *    keeps it valid after that, whatever the calls' sizes and paths.  Its
+ *    first moe_workspace_control_bytes() bytes are a control block that
+ *    records each call (see moe_workspace_status).
  *
  * Supported dimensions: H % 256 == 0, I % 64 == 0, Is % 64 == 0,
  * 1 <= K <= 8, K <= E <= 256, 0 <= T <= 2^22.
@@ -60,7 +66,10 @@ enum moe_status {
   MOE_ERR_WORKSPACE = 4, /* ws_bytes < moe_workspace_bytes(L, T)                */
   MOE_ERR_DEVICE = 5,    /* the current HIP device is not a gfx950              */
   MOE_ERR_LAUNCH = 6,    /* a HIP call failed; moe_last_error() has its text    */
-  MOE_ERR_MEMORY = 7     /* memory of the wrong kind or too small an allocation */
+  MOE_ERR_MEMORY = 7,    /* memory of the wrong kind or too small an allocation */
+  MOE_ERR_TIMEOUT = 8    /* moe_workspace_status: a wait inside the latest call's
+                            fused kernel timed out, so that call's outputs are
+                            invalid                                             */
 };
 
 /* One MoE layer: dimensions and device pointers to its seven parameters
@@ -241,6 +250,40 @@ int moe_forward_streamed(const moe_layer_t *L, const void *x, int64_t T, void *o
  * and results as moe_forward. */
 int moe_forward_traced(const moe_layer_t *L, const void *x, int64_t T, void *out,
                        void *ws, size_t ws_bytes, void *stream, void *const *events);
+
+/* Bytes of the control block at the start of every workspace (a constant;
+ * part of moe_workspace_bytes).  Host-only. */
+size_t moe_workspace_control_bytes(void);
+
+/* Status of the latest moe_route / moe_forward / moe_block_forward /
+ * moe_forward_traced / moe_load_balance / moe_forward_streamed call made with
+ * this workspace, once it has run: synchronises `stream` (the stream those
+ * calls were made on), stores in *timed_out_calls (if not NULL) how many
+ * calls on this workspace since it was zero-filled had a wait time out, then
+ * returns
+ *   MOE_OK           the call completed normally (or no call has used ws yet);
+ *   MOE_ERR_TIMEOUT  the call took the fused small-batch path (T <= 16) and one
+ *                    of that kernel's cross-workgroup waits gave up after its
+ *                    time budget: the kernel ran to completion, but the call's
+ *                    outputs are invalid.  The kernel runs one workgroup per
+ *                    compute unit and its waits need all of them resident at
+ *                    once, which holds when no other work occupies the
+ *                    device's compute units for the whole budget (0.25 s);
+ *                    a budget of 0 forces this status;
+ *   MOE_ERR_NULL / MOE_ERR_ALIGN / MOE_ERR_WORKSPACE for a bad ws pointer or
+ *                    ws_bytes < moe_workspace_control_bytes();
+ *   MOE_ERR_LAUNCH   if the copy of the status words or the
+ *                    synchronisation fails.
+ * The grouped path (T > 16) has no such waits and always reports MOE_OK. */
+int moe_workspace_status(const void *ws, size_t ws_bytes, void *stream, uint32_t *timed_out_calls);
+
+/* Diagnostic, process-wide: the time each cross-workgroup wait of the fused
+ * kernel may take before it gives up (default 250000 us), for calls made
+ * after this one.  0 makes a wait give up at its first unsuccessful poll (it
+ * forces the MOE_ERR_TIMEOUT path; every kernel still runs to completion and
+ * touches only its own arrays).  Returns the previous budget, or -1 (nothing
+ * changed) if us is outside [0, 60000000].  Host-only; no HIP call. */
+int64_t moe_set_wait_budget_us(int64_t us);
 
 /* Static text for a status code. */
 const char *moe_strerror(int code);

@@ -17,6 +17,7 @@ from dataclasses import dataclass
 
 import torch
 
+from . import _lib
 from ._lib import (EXPORTS, LIB_PATH, MoeError, MoeLayerT, lib, last_error,  # noqa: F401
                    strerror)
 
@@ -91,8 +92,10 @@ class MoeLayer:
         return int(lib.moe_workspace_bytes(self.desc, int(T)))
 
     def workspace(self, T: int, device=None) -> torch.Tensor:
+        """A new workspace for calls of up to T tokens, zero-filled as the ABI
+        requires before a workspace's first use."""
         dev = device or self.params["gate.weight"].device
-        return torch.empty(max(1, self.workspace_bytes(T)), dtype=torch.uint8, device=dev)
+        return torch.zeros(max(1, self.workspace_bytes(T)), dtype=torch.uint8, device=dev)
 
 
 def bits_to_device(bits, device="cuda") -> torch.Tensor:
@@ -100,6 +103,27 @@ def bits_to_device(bits, device="cuda") -> torch.Tensor:
     import numpy as np
     a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
     return torch.from_numpy(a).to(device).view(torch.bfloat16)
+
+
+def workspace_status(ws: torch.Tensor, stream=None, with_count: bool = False):
+    """Status of the latest call made with ``ws`` (moe_workspace_status):
+    0 (MOE_OK) or MOE_ERR_TIMEOUT; synchronises the stream.  With
+    ``with_count`` returns (status, calls on ws whose waits timed out)."""
+    import ctypes
+    n = ctypes.c_uint32(0)
+    rc = lib.moe_workspace_status(_ptr(ws), ws.numel(), _stream_handle(stream), ctypes.byref(n))
+    if rc not in (0, _lib.MOE_ERR_TIMEOUT):
+        raise MoeError(rc, "moe_workspace_status")
+    return (rc, int(n.value)) if with_count else rc
+
+
+def set_wait_budget_us(us: int) -> int:
+    """Budget of the fused kernel's cross-workgroup waits (moe_set_wait_budget_us);
+    returns the previous one."""
+    prev = int(lib.moe_set_wait_budget_us(int(us)))
+    if prev < 0:
+        raise ValueError(f"wait budget {us} us outside [0, 60000000]")
+    return prev
 
 
 def _check_x(x, layer):

@@ -20,11 +20,13 @@ MOE_ERR_WORKSPACE = 4
 MOE_ERR_DEVICE = 5
 MOE_ERR_LAUNCH = 6
 MOE_ERR_MEMORY = 7
+MOE_ERR_TIMEOUT = 8
 
 # Exported entry points, as include/moe.h declares them.
 EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_load_balance", "moe_forward",
            "moe_block_forward", "moe_rmsnorm", "moe_ranks", "moe_tile_experts", "moe_expert_cache_bytes", "moe_forward_streamed",
-           "moe_forward_traced", "moe_strerror", "moe_last_error")
+           "moe_forward_traced", "moe_workspace_control_bytes", "moe_workspace_status", "moe_set_wait_budget_us",
+           "moe_strerror", "moe_last_error")
 
 
 class MoeLayerT(ctypes.Structure):
@@ -83,6 +85,12 @@ def _load():
     lib.moe_ranks.restype = ctypes.c_int
     lib.moe_forward_traced.argtypes = [L, P, ctypes.c_int64, P, P, ctypes.c_size_t, P, P]
     lib.moe_forward_traced.restype = ctypes.c_int
+    lib.moe_workspace_control_bytes.argtypes = []
+    lib.moe_workspace_control_bytes.restype = ctypes.c_size_t
+    lib.moe_workspace_status.argtypes = [P, ctypes.c_size_t, P, ctypes.POINTER(ctypes.c_uint32)]
+    lib.moe_workspace_status.restype = ctypes.c_int
+    lib.moe_set_wait_budget_us.argtypes = [ctypes.c_int64]
+    lib.moe_set_wait_budget_us.restype = ctypes.c_int64
     lib.moe_strerror.argtypes = [ctypes.c_int]
     lib.moe_strerror.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []

@@ -193,12 +193,14 @@ struct Work {
   bf16_t* h;           // [T*K, I]
   bf16_t* h_sh;        // [T, Is]
   bf16_t* y;           // [T*K + T, H]  weighted expert outputs, routed slots then shared rows
-  float* psum;
+  float* psum;         // [nblk * E]  per router block: sum over its tokens of each expert's softmax probability
   int32_t* st_list;    // [E + 1]  streamed experts: touched experts ascending, then their count
   int32_t* st_slot;    // [E]      cache slot of each touched expert (-1 if untouched)
   int32_t* st_win_gu;  // [E][4]   per round: routed tile range and shared tile range (gate_up)
-  int32_t* st_win_dn;  // [E][4]   the same for the down projection         // [nblk * E]  per router block: sum over its tokens of each expert's softmax probability
+  int32_t* st_win_dn;  // [E][4]   the same for the down projection
   bf16_t* xn;          // [T, H]  RMSNorm of the sub-block input (block form)
+  uint32_t* ctl;       // control block at the start of the workspace (kCtlLast is written)
+  uint32_t call_tag;   // this call's tag
 };
 
 }  // namespace moe

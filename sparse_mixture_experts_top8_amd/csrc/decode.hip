@@ -67,11 +67,6 @@ constexpr int kXStride = 2048 + 8;       // LDS row stride of x, bf16 elements (
 constexpr int kBDepth = 2;               // gate/up blocks in flight per wave
 constexpr int kCDepth = 6;               // down-projection stages in flight per wave
 constexpr int kMaxCStages = 1 + 8 * 8;   // shared expert + one stage per expert touched by 8 tokens
-constexpr unsigned long long kWaitTicks = 25000000ull;  // 0.25 s of the 100 MHz clock
-
-// Control block layout (uint32 words).
-constexpr int kCtlError = 0;             // 0, or the call's tag once one of its waits timed out
-constexpr int kCtlFlags = 32;            // + x * kDecodeFlagStride: copy x of the arrival flags
 static_assert(kDecodeCtlWords >= kCtlFlags + kDecodeReplicas * kDecodeFlagStride, "control block too small");
 
 // Phase A weight fragment (plain load: the non-temporal hint measured slower
@@ -133,21 +128,28 @@ __device__ __forceinline__ void stores_complete() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Bounded wait: gives up after kWaitTicks (or soon after another wave of the
-// call gave up), records the call's tag in the error word and returns; indices
-// read from shared state are clamped by their users, so a timed-out wait
-// yields wrong numbers, never an out-of-bounds access.
+// Bounded wait: gives up once `budget` ticks of the 100 MHz wall clock have
+// passed (checked after the first miss and every 64 polls after it), or soon
+// after another wave of the call gave up; it then records the call's tag in
+// the error word (the first wave of the call to do so also counts the call in
+// the timed-out-calls word) and returns.  Indices read from shared state are clamped by
+// their users and every result the waits guard is read from LDS tables built
+// from the call's own (clamped) selections or through buffer resources bounded
+// by their arrays, so a timed-out wait yields wrong numbers, never an
+// out-of-bounds access, and the grid always drains.
 template <typename Ready>
-__device__ __forceinline__ void wait_until(Ready ready, uint32_t* err, uint32_t tag) {
+__device__ __forceinline__ void wait_until(Ready ready, uint32_t* ctl, uint32_t tag, unsigned long long budget) {
   if (!ready()) {
+    uint32_t* err = ctl + kCtlError;
     const unsigned long long t0 = wall_clock64();
     uint32_t n = 0;
     while (!ready()) {
       // A short back-off: every workgroup polls the same few lines, and
       // tighter polling only queues more requests in front of the writes.
       __builtin_amdgcn_s_sleep(4);
-      if ((++n & 63u) == 0u && (ld_cnt(err) == tag || wall_clock64() - t0 > kWaitTicks)) {
-        st_dev(err, tag);
+      if ((++n & 63u) == 1u && (ld_cnt(err) == tag || wall_clock64() - t0 > budget)) {
+        if (__hip_atomic_exchange(err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag)
+          __hip_atomic_fetch_add(ctl + kCtlTimeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
@@ -178,7 +180,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int nks = H / 128;            // k-steps in this wave's quarter of H
   const int kbeg = wave * (H / 4);
   uint32_t* ctl = a.ctl;
-  uint32_t* err = ctl + kCtlError;
   const uint32_t tag = (uint32_t)a.epoch;
   // This workgroup's XCD picks the copy of published data it polls.
   const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);   // HW_REG_XCC_ID[3:0]
@@ -197,9 +198,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __shared__ int s_tl[2][64];                   // experts touched by tokens 0-7 / 8-15, ascending (T > 8)
   __shared__ int s_U, s_U01;
 
-  // The error word is cleared at the start of every call (a timed-out wait
-  // sets it only after kWaitTicks, long after this store).
-  if (wg == 0 && tid == 0) st_dev(err, 0u);
+  // This call's tag goes into the control block's latest-call word; the error
+  // word is never cleared: it names the call whose wait timed out, so the
+  // latest call failed exactly when the two words are equal.
+  if (wg == 0 && tid == 0) st_dev(ctl + kCtlLast, tag);
   for (int i = tid; i < 256; i += kThreads) s_mask[i] = 0u;
 
   // ---------------- phase A: router rows and shared-expert rows ----------------
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         }
         return __ballot(!ok) == 0ull;
       };
-      wait_until(ready, err, tag);
+      wait_until(ready, ctl, tag, a.wait_ticks);
       float lv[NT][4];
 #pragma unroll
       for (int j = 0; j < NT; ++j)
@@ -634,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           for (int c = 0; c < 4; ++c) ok = ok && (4 * lane + c >= G || f[c] == tag);
           return __ballot(!ok) == 0ull;
         },
-        err, tag);
+        ctl, tag, a.wait_ticks);
   }
   __syncthreads();
 
@@ -700,9 +702,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 }  // namespace
 
 // Plain launch of one workgroup per CU: with the device otherwise idle every
-// workgroup is resident at once.  Should some not be (other kernels occupying
-// CUs), the bounded waits still let every wave finish, and the error word in
-// the workspace reports it.
+// workgroup is resident at once.  Should some not be (other kernels holding
+// CUs), the bounded waits still let every wave finish, and the control block
+// records the call as timed out (moe_workspace_status reports it).  A
+// cooperative launch would guarantee residency, but measured 38 us per
+// one-token call against 20.4 us for this one on MI355X.
 hipError_t launch_decode(const DecodeArgs& args, int grid, hipStream_t s) {
   hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kThreads), 0, s, args);
   return hipGetLastError();

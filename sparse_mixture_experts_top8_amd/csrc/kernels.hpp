@@ -77,6 +77,18 @@ int64_t router_partial_rows(int64_t T, int H);
 // Fused decode path (T <= kDecodeMaxT, H <= 2048, I <= 512, Is <= 512, and the
 // per-workgroup row shares of decode_fits).
 constexpr int kDecodeMaxT = 16;
+
+// Control block at the start of every workspace (uint32 words), shared by
+// both paths and written by nothing else, so its words keep their meaning
+// across calls of either path.  Tags are call-unique and never 0; a
+// zero-filled block holds no call's tag.
+constexpr int kCtlError = 0;   // tag of the latest call one of whose waits timed out
+constexpr int kCtlLast = 1;    // tag of the latest call that used the workspace
+constexpr int kCtlTimeouts = 2;  // calls one of whose waits timed out, since the block was zeroed
+constexpr int kCtlFlags = 32;  // fused path: + x * kDecodeFlagStride, copy x of the arrival flags
+// 100 MHz wall-clock ticks a fused-path wait may take before it gives up (0.25 s).
+constexpr unsigned long long kDefaultWaitTicks = 25000000ull;
+
 struct DecodeArgs {
   LayerArgs L;
   const bf16_t* x;      // [T, H]
@@ -95,6 +107,7 @@ struct DecodeArgs {
   int32_t* offsets_out; // route-only: [E + 1]
   int32_t* perm_out;    // route-only: [T*K]
   unsigned long long epoch;   // call-unique; its low 32 bits (never 0) tag this call's logits
+  unsigned long long wait_ticks;   // budget of each bounded wait (100 MHz ticks); 0: give up at the first miss
   const bf16_t* norm_w; // optional [H]: x is RMSNorm(x) with this weight (the sub-block form)
   float eps;            // RMSNorm epsilon
   const bf16_t* residual;  // optional [T, H]: out = bf16(residual + layer output)

@@ -36,6 +36,7 @@ int fail(int code, const char* fmt, ...) {
 constexpr int64_t kMaxTokens = int64_t(1) << 22;
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+constexpr size_t align256_c(size_t v) { return (v + 255) & ~size_t(255); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_dims(const moe_layer_t* L, int64_t T) {
@@ -60,6 +61,16 @@ struct Carve {
   size_t bytes;
 };
 
+// Both workspace layouts start with the same two regions: the control block
+// (error word, latest-call word, the fused path's arrival flags) and the fused
+// path's tagged logits sized for its largest batch.  Nothing else writes
+// them, so a word keeps its meaning whichever path ran last.
+constexpr size_t kCtlBytes = align256_c((size_t)moe::kDecodeCtlWords * 4);
+constexpr size_t kLogitTagBytes =
+    align256_c((size_t)moe::kDecodeReplicas * (size_t)(moe::kDecodeMaxT * 256 + 64) * 8);
+constexpr size_t kControlRegionBytes = kCtlBytes + kLogitTagBytes;
+static_assert(moe::kDecodeMaxT * 256 + 64 == 16 * 256 + 64, "tagged-logit region sized for the largest fused batch");
+
 // Workspace layout, each region 256-byte aligned.  With base == nullptr only
 // the size is computed.
 Carve carve(const moe_layer_t* L, int64_t T, char* base) {
@@ -72,6 +83,8 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
     return p;
   };
   Carve c{};
+  c.w.ctl = (uint32_t*)take(kCtlBytes);
+  take(kLogitTagBytes);
   c.w.topk_idx = (int32_t*)take(tk * 4);
   c.w.topk_w = (float*)take(tk * 4);
   c.w.gate_s = (float*)take(t * 4);
@@ -131,8 +144,8 @@ DecodeCarve carve_decode(const moe_layer_t* L, int64_t T, char* base) {
     return p;
   };
   DecodeCarve c{};
-  c.ctl = (uint32_t*)take(moe::kDecodeCtlWords * 4);
-  c.logits_t = (uint64_t*)take((size_t)moe::kDecodeReplicas * moe::decode_logit_stride((int)t) * 8);
+  c.ctl = (uint32_t*)take(kCtlBytes);
+  c.logits_t = (uint64_t*)take(kLogitTagBytes);   // copies at stride decode_logit_stride(T) <= that of kDecodeMaxT
   c.topk_idx = (int32_t*)take(tk * 4);
   c.topk_w = (float*)take(tk * 4);
   c.gate_s = (float*)take(t * 4);
@@ -166,6 +179,10 @@ unsigned long long next_epoch() {
   while ((uint32_t)e == 0u) e = ++g_epoch;
   return e;
 }
+
+// Budget of each bounded wait of the fused path, in ticks of the 100 MHz
+// wall clock (moe_set_wait_budget_us).
+std::atomic<unsigned long long> g_wait_ticks{moe::kDefaultWaitTicks};
 
 moe::LayerArgs layer_args(const moe_layer_t* L) {
   moe::LayerArgs a;
@@ -247,7 +264,15 @@ moe::DecodeArgs decode_args(const moe_layer_t* L, const void* x, int64_t T, cons
   a.h = c.h;
   a.h_sh = c.h_sh;
   a.epoch = next_epoch();
+  a.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
   return a;
+}
+
+// The grouped path's workspace view for one call (its tag in the control block).
+moe::Work grouped_work(const moe_layer_t* L, int64_t T, void* ws) {
+  moe::Work w = carve(L, T, (char*)ws).w;
+  w.call_tag = (uint32_t)next_epoch();
+  return w;
 }
 
 }  // namespace
@@ -305,8 +330,7 @@ int moe_route(const moe_layer_t* L, const void* x, int64_t T, int32_t* topk_idx,
     a.perm_out = perm;
     return launch_status(moe::launch_decode(a, dgrid, (hipStream_t)stream), "decode (route)");
   }
-  Carve c = carve(L, T, (char*)ws);
-  moe::Work w = c.w;
+  moe::Work w = grouped_work(L, T, ws);
   w.topk_idx = topk_idx;
   w.topk_w = topk_w;
   w.offsets = offsets;
@@ -336,7 +360,7 @@ int moe_load_balance(const moe_layer_t* L, const void* x, int64_t T, float* lb, 
   int cus = 0, dgrid = 0;
   if ((rc = device_check(&cus, &dgrid)) != MOE_OK) return rc;
   // Always the grouped path's router and dispatch (any T).
-  const moe::Work w = carve(L, T, (char*)ws).w;
+  const moe::Work w = grouped_work(L, T, ws);
   const moe::LayerArgs a = layer_args(L);
   hipStream_t s = (hipStream_t)stream;
   const int t = (int)T;
@@ -374,7 +398,7 @@ int forward_impl(const moe_layer_t* L, const void* x, int64_t T, void* out, void
       if ((rc = mark(i)) != MOE_OK) return rc;
     return MOE_OK;
   }
-  const moe::Work w = carve(L, T, (char*)ws).w;
+  const moe::Work w = grouped_work(L, T, ws);
   const moe::LayerArgs a = layer_args(L);
   const int t = (int)T;
   const bf16_t* xin = (const bf16_t*)x;
@@ -527,7 +551,7 @@ int moe_forward_streamed(const moe_layer_t* L, const void* x, int64_t T, void* o
   if ((rc = host_span(L->gate_up_w, (size_t)E * gu, "gate_up_w", &host_gu)) != MOE_OK) return rc;
   if ((rc = host_span(L->down_w, (size_t)E * dn, "down_w", &host_dn)) != MOE_OK) return rc;
   const int64_t R = (std::min<int64_t>(E, T * L->top_k) + C - 1) / C;
-  const moe::Work w = carve(L, T, (char*)ws).w;
+  const moe::Work w = grouped_work(L, T, ws);
   moe::LayerArgs a = layer_args(L);
   char* slot_gu = (char*)cache;
   char* slot_dn = slot_gu + (size_t)C * gu;
@@ -552,6 +576,34 @@ int moe_forward_streamed(const moe_layer_t* L, const void* x, int64_t T, void* o
   return launch_status(moe::launch_combine(a, t, w, (bf16_t*)out, s), "combine");
 }
 
+size_t moe_workspace_control_bytes(void) { return kControlRegionBytes; }
+
+int moe_workspace_status(const void* ws, size_t ws_bytes, void* stream, uint32_t* timed_out_calls) {
+  if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < kControlRegionBytes)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, fewer than its %zu-byte control region", ws_bytes,
+                kControlRegionBytes);
+  uint32_t w[3] = {0u, 0u, 0u};
+  hipStream_t s = (hipStream_t)stream;
+  int rc = launch_status(hipMemcpyAsync(w, ws, sizeof w, hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+  if (rc != MOE_OK) return rc;
+  if ((rc = launch_status(hipStreamSynchronize(s), "hipStreamSynchronize")) != MOE_OK) return rc;
+  static_assert(moe::kCtlError == 0 && moe::kCtlLast == 1 && moe::kCtlTimeouts == 2, "status words");
+  if (timed_out_calls) *timed_out_calls = w[2];
+  if (w[1] != 0u && w[0] == w[1])
+    return fail(MOE_ERR_TIMEOUT, "a cross-workgroup wait of the latest call on this workspace timed out; "
+                                 "its outputs are invalid");
+  return MOE_OK;
+}
+
+int64_t moe_set_wait_budget_us(int64_t us) {
+  const unsigned long long prev = g_wait_ticks.load();
+  if (us < 0 || us > 60000000) return -1;
+  g_wait_ticks.store((unsigned long long)us * 100ull);
+  return (int64_t)(prev / 100ull);
+}
+
 const char* moe_strerror(int code) {
   switch (code) {
     case MOE_OK: return "ok";
@@ -562,6 +614,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_DEVICE: return "current device is not a gfx950";
     case MOE_ERR_LAUNCH: return "a HIP call failed";
     case MOE_ERR_MEMORY: return "memory of the wrong kind or extent";
+    case MOE_ERR_TIMEOUT: return "a wait inside the fused kernel timed out; that call's outputs are invalid";
     default: return "unknown status code";
   }
 }

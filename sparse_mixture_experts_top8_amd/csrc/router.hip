@@ -49,8 +49,12 @@ constexpr int kMaxRouterCols = 260;      // router_cols(256)
 template <int kTB>
 __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
                                                             int ksplit, float* __restrict__ part,
-                                                            int* __restrict__ hist_zero, int hist_n) {
+                                                            int* __restrict__ hist_zero, int hist_n,
+                                                            uint32_t* __restrict__ ctl, uint32_t tag) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // The call's tag goes into the workspace's latest-call word (this path has
+  // no waits, so the call never matches the error word).
+  if (ctl && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) ctl[kCtlLast] = tag;
   // The selection adds its pairs to these block histograms (integer atomics):
   // they start at zero.
   if (hist_zero) {
@@ -417,11 +421,14 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
   int* hz = block_hist ? w.blk_counts : nullptr;
   const int hn = router_blocks(T) * L.E;
   if (tile == 32)
-    hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn);
+    hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+                       w.call_tag);
   else if (tile == 64)
-    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn);
+    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+                       w.call_tag);
   else
-    hipLaunchKernelGGL(router_logits_kernel<8>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn);
+    hipLaunchKernelGGL(router_logits_kernel<8>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+                       w.call_tag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (per_token)

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_codes():
-    for code in range(8):
+    for code in range(9):
         assert _lib.strerror(code) and _lib.strerror(code) != "unknown status code"
     assert _lib.strerror(99) == "unknown status code"
 
@@ -210,3 +210,29 @@ def test_tile_experts_checks():
     assert _validate(L) == _lib.MOE_OK
     L.experts_tiled = 3
     assert _validate(L) == _lib.MOE_ERR_SHAPE and "experts_tiled" in _lib.last_error()
+
+
+def test_workspace_control_block_and_status_checks():
+    # Every workspace starts with the same control block, whatever the path
+    # and batch size, and the status query rejects bad arguments before any
+    # HIP call.
+    cb = _lib.lib.moe_workspace_control_bytes()
+    assert cb > 0 and cb % 256 == 0
+    for dims in [(2048, 256, 8, 512, 512), (256, 16, 4, 64, 64)]:
+        for T in (1, 16, 17, 4096):
+            assert _lib.lib.moe_workspace_bytes(_layer(*dims), T) > cb
+    st = _lib.lib.moe_workspace_status
+    assert st(None, cb, None, None) == _lib.MOE_ERR_NULL
+    assert st(FAKE + 4, cb, None, None) == _lib.MOE_ERR_ALIGN
+    assert st(FAKE, cb - 1, None, None) == _lib.MOE_ERR_WORKSPACE
+    assert "control" in _lib.last_error()
+
+
+def test_wait_budget_setter():
+    sb = _lib.lib.moe_set_wait_budget_us
+    prev = sb(250000)
+    assert prev == 250000            # the documented default
+    assert sb(0) == 250000
+    assert sb(-1) == -1 and sb(60000001) == -1   # rejected, nothing changed
+    assert sb(250000) == 0
+    assert sb(250000) == 250000
