@@ -46,3 +46,26 @@ def test_more_than_one_gpu_is_refused():
                        stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stdout
+
+
+def test_attainable_fraction_is_the_larger_roofline_time():
+    # One-token decode: memory time (57.7 MB at 8 TB/s = 7.2 us) dominates the
+    # compute time (57.7 MFLOP at 2.5 PFLOP/s = 0.023 us); a 21.19 us step is
+    # then 7.21 / 21.19 = 34 % of the attainable roofline, the HBM fraction.
+    nbytes, flops = bench.step_work(mi.FULL, 1, 8)
+    sec = 21.19e-6
+    frac = bench.attainable_frac(nbytes, flops, sec)
+    assert abs(frac - nbytes / 8e12 / sec) < 1e-12
+    assert abs(frac - 0.3403) < 1e-3
+    # A compute-bound step (above the ridge) takes the MFMA time instead.
+    frac_c = bench.attainable_frac(1e6, 2.5e15, 2.0)
+    assert abs(frac_c - 0.5) < 1e-12
+
+
+def test_load_stats_of_a_zipf_law():
+    import numpy as np
+    loads = np.round(1e4 * np.arange(1, 257, dtype=np.float64) ** -1.1)
+    s = bench.load_stats(np.random.default_rng(0).permutation(loads))
+    assert abs(s["loglog_slope"] + 1.1) < 0.02
+    assert s["max"] == 10000 and s["sorted_loads"][0] == 10000
+    assert abs(s["max_over_mean"] - 10000 / loads.mean()) < 1e-2
