@@ -285,6 +285,21 @@ int moe_workspace_status(const void *ws, size_t ws_bytes, void *stream, uint32_t
  * changed) if us is outside [0, 60000000].  Host-only; no HIP call. */
 int64_t moe_set_wait_budget_us(int64_t us);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and the same results, bit for bit, with the workspace replaced
+ * by a static scratch array of 16 MiB that the library holds on each device it
+ * runs on until the process ends (enough for T up to 244 at H 2048, E 256,
+ * K 8, I = Is = 512; moe_workspace_bytes(L, T) must be at most 16 MiB, else
+ * MOE_ERR_WORKSPACE and nothing is enqueued).  No hipMalloc, hipFree or other
+ * allocating call.  The first call on a device also enqueues, on `stream`, a
+ * kernel that zero-fills the scratch's control block.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (other streams, or
+ * other host threads) race and must be serialised by the caller.  Other
+ * arguments and errors as moe_forward; a fused-kernel timeout (see
+ * moe_workspace_status) is not reported through this entry point. */
+int moe_forward_noalloc(const moe_layer_t *L, const void *x, int64_t T, void *out, void *stream);
+
 /* Static text for a status code. */
 const char *moe_strerror(int code);
 

@@ -146,6 +146,19 @@ def forward(x: torch.Tensor, layer: MoeLayer, out: torch.Tensor | None = None,
     return out
 
 
+def forward_noalloc(x: torch.Tensor, layer: MoeLayer, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """moe_forward_noalloc: the layer with the library's static scratch in
+    place of a workspace (no device allocation inside the call)."""
+    _check_x(x, layer)
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib.moe_forward_noalloc(layer.desc, _ptr(x), x.shape[0], _ptr(out), _stream_handle(stream))
+    if rc != 0:
+        raise MoeError(rc, "moe_forward_noalloc")
+    return out
+
+
 PHASES = ("router", "dispatch", "gate_up", "down", "combine")
 
 

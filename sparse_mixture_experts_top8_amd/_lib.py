@@ -26,7 +26,7 @@ MOE_ERR_TIMEOUT = 8
 EXPORTS = ("moe_workspace_bytes", "moe_validate", "moe_route", "moe_load_balance", "moe_forward",
            "moe_block_forward", "moe_rmsnorm", "moe_ranks", "moe_tile_experts", "moe_expert_cache_bytes", "moe_forward_streamed",
            "moe_forward_traced", "moe_workspace_control_bytes", "moe_workspace_status", "moe_set_wait_budget_us",
-           "moe_strerror", "moe_last_error")
+           "moe_forward_noalloc", "moe_strerror", "moe_last_error")
 
 
 class MoeLayerT(ctypes.Structure):
@@ -91,6 +91,8 @@ def _load():
     lib.moe_workspace_status.restype = ctypes.c_int
     lib.moe_set_wait_budget_us.argtypes = [ctypes.c_int64]
     lib.moe_set_wait_budget_us.restype = ctypes.c_int64
+    lib.moe_forward_noalloc.argtypes = [L, P, ctypes.c_int64, P, P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
     lib.moe_strerror.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []

@@ -578,6 +578,79 @@ int moe_forward_streamed(const moe_layer_t* L, const void* x, int64_t T, void* o
 
 size_t moe_workspace_control_bytes(void) { return kControlRegionBytes; }
 
+}  // extern "C"
+
+// ---- moe_forward without a caller workspace ----
+// Scratch of the no-allocation entry point: one array per device (each GPU the
+// library runs on holds its own copy until the process ends).  Host code uses
+// only the device address hipGetSymbolAddress gives for the current device,
+// never the array's name.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void scratch_clear_kernel(uint32_t* p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[64];
+
+// The scratch's device address on the current device, set up on the first
+// call made on that device: its control block is zero-filled once by a kernel
+// on `s` (the fused path's words must start holding no call's tag; nothing
+// else in it needs clearing, every call writes what it later reads).
+int scratch_for_device(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "device index %d out of range", dev);
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&] {
+    void* p = nullptr;
+    sl.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (sl.err == hipSuccess && p) {
+      hipLaunchKernelGGL(scratch_clear_kernel, dim3(64), dim3(256), 0, s, (uint32_t*)p, kControlRegionBytes / 4);
+      sl.err = hipGetLastError();
+    }
+    if (sl.err == hipSuccess) sl.ptr = p;
+  });
+  if (sl.err != hipSuccess || !sl.ptr)
+    return fail(MOE_ERR_LAUNCH, "static scratch on device %d: %s", dev, hipGetErrorString(sl.err));
+  *out = sl.ptr;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_layer_t* L, const void* x, int64_t T, void* out, void* stream) {
+  int rc = check_dims(L, T);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_weights(L)) != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x) return fail(MOE_ERR_NULL, "x is NULL");
+  if (!out) return fail(MOE_ERR_NULL, "out is NULL");
+  if (!aligned16(x)) return fail(MOE_ERR_ALIGN, "x is not 16-byte aligned");
+  if (!aligned16(out)) return fail(MOE_ERR_ALIGN, "out is not 16-byte aligned");
+  const size_t need = workspace_need(L, T);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "T = %lld needs %zu bytes of scratch; the static scratch holds %zu",
+                (long long)T, need, kScratchBytes);
+  int cus = 0;
+  if ((rc = device_check(&cus)) != MOE_OK) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_for_device((hipStream_t)stream, &ws)) != MOE_OK) return rc;
+  return forward_impl(L, x, T, out, ws, kScratchBytes, stream, nullptr, nullptr, 0.f);
+}
+
 int moe_workspace_status(const void* ws, size_t ws_bytes, void* stream, uint32_t* timed_out_calls) {
   if (!ws) return fail(MOE_ERR_NULL, "workspace is NULL");
   if (!aligned16(ws)) return fail(MOE_ERR_ALIGN, "workspace is not 16-byte aligned");

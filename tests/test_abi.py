@@ -236,3 +236,19 @@ def test_wait_budget_setter():
     assert sb(-1) == -1 and sb(60000001) == -1   # rejected, nothing changed
     assert sb(250000) == 0
     assert sb(250000) == 250000
+
+
+def test_noalloc_entry_point_checks():
+    # Argument checks and the scratch limit come before any HIP call.
+    L = _layer()
+    fn = _lib.lib.moe_forward_noalloc
+    assert fn(L, None, 0, None, None) == _lib.MOE_OK
+    assert fn(L, None, 4, FAKE, None) == _lib.MOE_ERR_NULL
+    assert fn(L, FAKE, 4, None, None) == _lib.MOE_ERR_NULL
+    assert fn(L, FAKE + 2, 4, FAKE, None) == _lib.MOE_ERR_ALIGN
+    assert fn(L, FAKE, -1, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert fn(_layer(H=100), FAKE, 4, FAKE, None) == _lib.MOE_ERR_SHAPE
+    # 16 MiB of scratch: 244 tokens fit at full shape, 245 do not.
+    assert _lib.lib.moe_workspace_bytes(L, 244) <= 16 << 20 < _lib.lib.moe_workspace_bytes(L, 245)
+    assert fn(L, FAKE, 245, FAKE, None) == _lib.MOE_ERR_WORKSPACE
+    assert "static scratch" in _lib.last_error()
