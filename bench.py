@@ -618,12 +618,18 @@ def main():
     if args.copy_probe:
         return copy_probe()
 
+    # The shader clock levels come from rocm-smi, queried before this process
+    # touches the GPU (a child started after that could not run under a
+    # profiler's preloaded library); only for the default line.
+    clock_before_gpu_use = gpu_clock() if args.workload is None else None
+
     import torch
 
     import moe_inputs as mi
     import sparse_mixture_experts_top8_amd as moe
 
     prop = torch.cuda.get_device_properties(0)
+    sclk = clock_before_gpu_use
     log(f"device {prop.name} ({getattr(prop, 'gcnArchName', '?')}), {prop.multi_processor_count} CUs")
     t_all = time.time()
     base_bits = mi.workload_layer(mi.WORKLOADS[HEADLINE])   # all workloads share the layer seed
@@ -674,7 +680,7 @@ def main():
         "config": {"workload": h["workload"], "tokens_per_step": wl.T, "layers_rotated": h["layers_rotated"],
                    "weights": "seeded N(0,0.02) bf16",
                    "expert_layout": "row-major" if args.row_major else "mfma-tile",
-                   "device": prop.name, "cus": prop.multi_processor_count, "sclk": gpu_clock()},
+                   "device": prop.name, "cus": prop.multi_processor_count, "sclk": sclk},
         "roofline": h["roofline"],
         "layer": h["layer"],
         "repeats_ms": h["repeats_ms"],

@@ -92,7 +92,8 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 // from each lane's four logits of experts 4 lane + c: order by descending
 // logit, ties to the lower expert index; lane k < K receives the k-th index
 // and its weight, the softmax over the selected logits (equal to the full
-// softmax renormalised over them), its denominator summed in rank order.
+// softmax renormalised over them), its denominator summed in rank order
+// (lanes >= K receive a weight they do not use).
 //
 // Each lane first sorts its four keys (descending, lower c first among equal
 // keys), so its best remaining candidate is always its head.  A pick is the
@@ -124,9 +125,8 @@ __device__ __forceinline__ void topk_select(const float (&lv)[NT][4], int E, int
     hc[j] = (uint32_t)(c[0] | (c[1] << 2) | (c[2] << 4) | (c[3] << 6));
   }
   uint32_t my_key[NT], my_idx[NT], first_key[NT];
-  float den[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) { my_key[j] = 0u; my_idx[j] = 0u; first_key[j] = 0u; den[j] = 0.f; }
+  for (int j = 0; j < NT; ++j) { my_key[j] = 0u; my_idx[j] = 0u; first_key[j] = 0u; }
   for (int k = 0; k < K; ++k) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -140,14 +140,19 @@ __device__ __forceinline__ void topk_select(const float (&lv)[NT][4], int E, int
       hk[j][3] = won ? 0u : hk[j][3];
       hc[j] = won ? hc[j] >> 2 : hc[j];
       if (k == 0) first_key[j] = m;
-      den[j] += __expf(key_logit(m) - key_logit(first_key[j]));
       if (lane == k) { my_key[j] = m; my_idx[j] = 4u * (uint32_t)wl + wc; }
     }
   }
+  // Lane k < K holds the k-th pick: its softmax numerator is formed in every
+  // lane at once, and the denominator summed in rank order from them (the
+  // exponentials stay off the selection's dependent chain).
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
+    const float num = lane < K ? __expf(key_logit(my_key[j]) - key_logit(first_key[j])) : 0.f;
+    float den = 0.f;
+    for (int k = 0; k < K; ++k) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(num), k));
     idx_out[j] = clamp_expert((int)my_idx[j], E);
-    w_out[j] = __expf(key_logit(my_key[j]) - key_logit(first_key[j])) / den[j];
+    w_out[j] = num / den;
   }
 }
 

@@ -67,6 +67,9 @@ constexpr int kXStride = 2048 + 8;       // LDS row stride of x, bf16 elements (
 constexpr int kBDepth = 2;               // gate/up blocks in flight per wave
 constexpr int kCDepth = 6;               // down-projection stages in flight per wave
 constexpr int kMaxCStages = 1 + 8 * 8;   // shared expert + one stage per expert touched by 8 tokens
+constexpr int kLateMaxPairs = 2;         // shared (gate, up) pairs per workgroup on the wave-3 path
+constexpr int kLateRows = 1 + 2 * kLateMaxPairs;   // the gate row, then the pairs
+constexpr int kLateChunks = 4;           // 512-element chunks of a row (H <= 2048)
 static_assert(kDecodeCtlWords >= kCtlFlags + kDecodeReplicas * kDecodeFlagStride, "control block too small");
 
 // Phase A weight fragment (plain load: the non-temporal hint measured slower
@@ -94,9 +97,6 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutside = 0x80000000u;   // out of range even after adding a k offset
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ float ld_pub_f(rsrc_t r, uint32_t off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16));
 }
 // h after its hand-off: an ordinary (L2-cacheable) load.  No CU reads h
 // before the hand-off in a call, and the caches hold no copies from earlier
@@ -129,14 +129,15 @@ __device__ __forceinline__ void stores_complete() {
 }
 
 // Bounded wait: gives up once `budget` ticks of the 100 MHz wall clock have
-// passed (checked after the first miss and every 64 polls after it), or soon
-// after another wave of the call gave up; it then records the call's tag in
-// the error word (the first wave of the call to do so also counts the call in
-// the timed-out-calls word) and returns.  Indices read from shared state are clamped by
-// their users and every result the waits guard is read from LDS tables built
-// from the call's own (clamped) selections or through buffer resources bounded
-// by their arrays, so a timed-out wait yields wrong numbers, never an
-// out-of-bounds access, and the grid always drains.
+// passed (checked at every unsuccessful poll: a scalar clock read, no memory
+// access), or soon after another wave of the call gave up (the error word is
+// read every 64 polls); it then records the call's tag in the error word (the
+// first wave of the call to do so also counts the call in the
+// timed-out-calls word) and returns.  Indices read from shared state are
+// clamped by their users and every result the waits guard is read from LDS
+// tables built from the call's own (clamped) selections or through buffer
+// resources bounded by their arrays, so a timed-out wait yields wrong
+// numbers, never an out-of-bounds access, and the grid always drains.
 template <typename Ready>
 __device__ __forceinline__ void wait_until(Ready ready, uint32_t* ctl, uint32_t tag, unsigned long long budget) {
   if (!ready()) {
@@ -147,7 +148,7 @@ __device__ __forceinline__ void wait_until(Ready ready, uint32_t* ctl, uint32_t 
       // A short back-off: every workgroup polls the same few lines, and
       // tighter polling only queues more requests in front of the writes.
       __builtin_amdgcn_s_sleep(4);
-      if ((++n & 63u) == 1u && (ld_cnt(err) == tag || wall_clock64() - t0 > budget)) {
+      if (wall_clock64() - t0 > budget || ((++n & 63u) == 0u && ld_cnt(err) == tag)) {
         if (__hip_atomic_exchange(err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag)
           __hip_atomic_fetch_add(ctl + kCtlTimeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -210,12 +211,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // shared gate row (when it owns inner rows), then (gate, up) row pairs; the
   // host guarantees they fit one 16-row tile.  The weight loads go out first,
   // then x is staged in LDS (every workgroup keeps all of x there).
+  //
+  // With fewer tokens than waves (T <= 3) wave 3 routes no token, so the
+  // shared rows leave the tile: after the router tile, wave 3 requests them
+  // (the gate row and the pairs, whole rows, coalesced) and forms h_sh with
+  // VALU dot products while the other waves poll the logits.  The router
+  // tile then waits for router rows only, which puts the logit exchange
+  // earlier.
+  const int s_lo = (int)((long long)wg * Is / G), s_hi = (int)((long long)(wg + 1) * Is / G);
+  const int n_s = s_hi - s_lo;
+  const bool late_shared = T < kWaves && n_s <= kLateMaxPairs;
+  const bool late_wave = late_shared && wave == kWaves - 1 && n_s > 0;
   {
     const int r_lo = (int)((long long)wg * (E + 1) / G), r_hi = (int)((long long)(wg + 1) * (E + 1) / G);
-    const int s_lo = (int)((long long)wg * Is / G), s_hi = (int)((long long)(wg + 1) * Is / G);
-    const int n_r = r_hi - r_lo, n_s = s_hi - s_lo;
-    const int p0 = n_r + (n_s > 0 ? 1 : 0);            // first (gate, up) pair row
-    const int nrow = p0 + 2 * n_s;
+    const int n_r = r_hi - r_lo;
+    const int p0 = late_shared ? n_r : n_r + (n_s > 0 ? 1 : 0);   // first (gate, up) pair row
+    const int nrow = late_shared ? n_r : p0 + 2 * n_s;
     u32x4 af[kMaxHSteps];
     if (nrow > 0) {
       const int mr = min(m, nrow - 1);
@@ -328,6 +339,70 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
   }
 
+  // ---------------- wave 3: shared rows (T <= 3) ----------------
+  // Dot products of the gate row and the (gate, up) pairs with each token's x
+  // (fixed per-lane order, then a fixed-order wave sum), then
+  // h_sh = sigma(zg) SiLU(g) u as in the tile path; published like the rest
+  // of h (complete before the hand-off).
+  if (late_wave) {
+    // Requested only now, after this workgroup's router rows: the router loads
+    // of every workgroup (up to ~1 us apart in start time) reach memory first,
+    // and these 4 MB (over the grid) use the otherwise idle time of the logit
+    // exchange.  Lane l reads elements 8 l + 512 j .. + 7 of each row.
+    u32x4 shw[kLateRows][kLateChunks];
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < kLateRows; ++r) {
+      const int p = (r - 1) >> 1;
+      const bf16_t* rp = r == 0 ? L.sh_expert_gate
+                                : (((r - 1) & 1) ? L.sh_up_w : L.sh_gate_w) + (size_t)(s_lo + min(p, n_s - 1)) * H;
+#pragma unroll
+      for (int j = 0; j < kLateChunks; ++j) {
+        const int e = 8 * lane + 512 * j;
+        shw[r][j] = (r == 0 || p < n_s) && e < H ? ldw(rp + e) : z4;
+      }
+    }
+    float acc[kLateRows][kWaves - 1];
+#pragma unroll
+    for (int r = 0; r < kLateRows; ++r)
+#pragma unroll
+      for (int t = 0; t < kWaves - 1; ++t) acc[r][t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kLateChunks; ++j) {
+      const int e = 8 * lane + 512 * j;
+      if (e < H) {
+#pragma unroll
+        for (int t = 0; t < kWaves - 1; ++t) {
+          if (t < T) {
+            const u32x4 xv = ld_lds16(s_x + t * kXStride + e);
+#pragma unroll
+            for (int r = 0; r < kLateRows; ++r)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                acc[r][t] += bf16_to_f32(shw[r][j][i] & 0xFFFFu) * bf16_to_f32(xv[i] & 0xFFFFu);
+                acc[r][t] += bf16_to_f32(shw[r][j][i] >> 16) * bf16_to_f32(xv[i] >> 16);
+              }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kWaves - 1; ++t) {
+      if (t < T) {
+        float sum[kLateRows];
+#pragma unroll
+        for (int r = 0; r < kLateRows; ++r) sum[r] = wave_sum_f32(acc[r][t]);
+        const float zg = a.L.logits_bf16 ? round_bf16(sum[0]) : sum[0];
+#pragma unroll
+        for (int p = 0; p < kLateMaxPairs; ++p)
+          if (p < n_s && lane == p) {
+            const float hv = sigmoidf_(zg) * siluf_(sum[1 + 2 * p]) * sum[2 + 2 * p];
+            st_dev(a.h_sh + (size_t)t * Is + s_lo + p, (bf16_t)f32_to_bf16(hv));
+          }
+      }
+    }
+  }
+
   // ---------------- phase K: top-K selections into LDS ----------------
   // Wave w handles tokens w, w + 4, ... (NT of them, lane: experts 4 lane ..
   // 4 lane + 3): it polls their tagged logits (its XCD's copy) until every one
@@ -336,7 +411,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const rsrc_t r_lt = make_rsrc(a.logits_t + (size_t)xcc * lstride, (size_t)T * 256 * 8);
     auto run = [&](auto nt_tag) {
       constexpr int NT = decltype(nt_tag)::value;
-      uint64_t sl[NT][4];
+      // Each poll also takes the logits out of the words it checks: the last
+      // one, which succeeded (or gave up), leaves them in lv.
+      float lv[NT][4];
       auto ready = [&] {
         bool ok = true;
 #pragma unroll
@@ -349,18 +426,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             // One 64-bit load: value and tag come from the same store.
             const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(
                 r_lt, in ? 8u * (uint32_t)(t * 256 + 64 * c + lane) : kOutside, 0, 16);
-            sl[j][c] = ((uint64_t)w2[1] << 32) | w2[0];
-            ok = ok && (!in || (uint32_t)sl[j][c] == tag);
+            ok = ok && (!in || w2[0] == tag);
+            lv[j][c] = __uint_as_float(w2[1]);
           }
         }
         return __ballot(!ok) == 0ull;
       };
       wait_until(ready, ctl, tag, a.wait_ticks);
-      float lv[NT][4];
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) lv[j][c] = __uint_as_float((uint32_t)(sl[j][c] >> 32));
       int ix[NT];
       float wv[NT];
       topk_select<NT>(lv, E, K, lane, ix, wv);
@@ -380,14 +452,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       else run(std::integral_constant<int, 4>{});
     }
   }
-  __syncthreads();
+  // One token of a forward call: wave 0 made every selection and builds the
+  // lists itself (its own LDS writes are visible to its later reads), so no
+  // barrier separates the two phases and wave 3's shared rows only have to be
+  // done by the barrier after phase L.
+  const bool solo = T == 1 && !a.route_only;
+  if (!solo) __syncthreads();
 
   // ---------------- phase L: per-expert pair lists in LDS ----------------
   // From the token masks per expert (set with the selections), wave 0 forms
   // the offsets and the touched list (ascending expert) from one scan (low
   // half: pair counts, high half: touched flags), then each pair's slot: its
   // expert's offset plus the number of earlier tokens with that expert.
-  if (wave == 0) {
+  //
+  // One token (forward): the K selections are distinct and each holds one
+  // pair, so the touched list is the selections in ascending order: lane k
+  // (k < K) finds the rank of its expert among them, which is its slot; the
+  // offsets of a touched expert and of the expert after it are that rank and
+  // rank + 1 (the only offsets phases B and C read).
+  if (solo && wave == 0) {
+    const int ek = lane < K ? s_tidx[lane] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < K; ++j) rank += __builtin_amdgcn_readlane(ek, j) < ek ? 1 : 0;
+    if (lane < K) {
+      s_touched[rank] = ek;
+      s_list[rank] = lane;
+      s_off[ek] = rank;
+    }
+    if (lane < K) s_off[ek + 1] = rank + 1;
+    if (lane == 0) { s_U = K; s_U01 = 0; }
+  } else if (wave == 0) {
     // Second scan: touched flags per token group (tokens 0-7 low half, 8-15
     // high half) for phase C with T > 8.
     int v4[4], g4[4], run = 0, grun = 0;
