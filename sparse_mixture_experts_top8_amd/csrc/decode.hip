@@ -339,17 +339,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // ---------------- wave 3: shared rows (T <= 3) ----------------
-  // Dot products of the gate row and the (gate, up) pairs with each token's x
-  // (fixed per-lane order, then a fixed-order wave sum), then
-  // h_sh = sigma(zg) SiLU(g) u as in the tile path; published like the rest
-  // of h (complete before the hand-off).
+  // ---------------- wave 3: shared rows (T <= 3), requested ----------------
+  // Requested only now, after this workgroup's router rows: the router loads
+  // of every workgroup (up to ~1 us apart in start time) reach memory first,
+  // and these 4 MB (over the grid) use the otherwise idle time of the logit
+  // exchange.  Lane l reads elements 8 l + 512 j .. + 7 of each row.  They
+  // are consumed at the start of phase B, so the lists barrier never waits
+  // for them.
+  u32x4 shw[kLateRows][kLateChunks];
   if (late_wave) {
-    // Requested only now, after this workgroup's router rows: the router loads
-    // of every workgroup (up to ~1 us apart in start time) reach memory first,
-    // and these 4 MB (over the grid) use the otherwise idle time of the logit
-    // exchange.  Lane l reads elements 8 l + 512 j .. + 7 of each row.
-    u32x4 shw[kLateRows][kLateChunks];
     const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < kLateRows; ++r) {
@@ -362,6 +360,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         shw[r][j] = (r == 0 || p < n_s) && e < H ? ldw(rp + e) : z4;
       }
     }
+  }
+  // Dot products of the gate row and the (gate, up) pairs with each token's x
+  // (fixed per-lane order, then a fixed-order wave sum), then
+  // h_sh = sigma(zg) SiLU(g) u as in the tile path; published like the rest
+  // of h (complete before the hand-off).
+  auto late_shared_rows = [&] {
     float acc[kLateRows][kWaves - 1];
 #pragma unroll
     for (int r = 0; r < kLateRows; ++r)
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           }
       }
     }
-  }
+  };
 
   // ---------------- phase K: top-K selections into LDS ----------------
   // Wave w handles tokens w, w + 4, ... (NT of them, lane: experts 4 lane ..
@@ -663,6 +667,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
     };
     static_assert(kBDepth == 2, "the loop below is unrolled for two stages");
+    if (late_wave) late_shared_rows();
     issue(wa[0], 0);
     issue(wa[1], 1);
     // Phase C's B operands: for every stage and tile column the row of h
