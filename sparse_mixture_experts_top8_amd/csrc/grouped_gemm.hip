@@ -32,7 +32,12 @@
 // contiguous bytes of a weight row per step.
 //
 // LDS rows of the activation tile are 128 bytes; the 16-byte chunk c of row r
-// is stored at chunk c ^ (r & 7).  LDS is read with inline ds_read_b128 and the
+// is stored at chunk c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  A
+// ds_read_b128 of an MFMA operand reads rows 0 .. 15 of a block, one chunk
+// column each: with 64 four-byte banks two consecutive rows share the bank
+// space, and the term from bit 3 gives rows r and r + 8 different chunks (a
+// plain r & 7 serves them from the same banks: MI355X counted bank conflicts
+// on half of the GEMM's LDS cycles).  LDS is read with inline ds_read_b128 and the
 // load counter waited for explicitly: the compiler would otherwise drain every
 // outstanding direct-to-LDS load before any LDS access.  For the same reason
 // every load in the loop is issued unconditionally, so the counts the
@@ -76,6 +81,8 @@ constexpr uint32_t kOutside = 0x80000000u;
 constexpr int kNonTemporal = 2;   // buffer-load cache policy bit: non-temporal (streamed once)
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// Stored chunk of chunk 0 of activation-tile row r (the same in every 16-row block).
+__device__ __forceinline__ int lds_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int OFF>
 __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
@@ -177,12 +184,12 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
   // ---- activation sources: direct-to-LDS instruction j (0..kADma-1) of
   // wave w writes 16-byte unit p = 64 (4 j + w) + lane, i.e. row
   // r = 8 (4 j + w) + lane / 8, stored chunk lane % 8, holding the global
-  // chunk (lane % 8) ^ (r & 7).
+  // chunk (lane % 8) ^ swz(r).
   const bf16_t* a_src[kADma];
 #pragma unroll
   for (int j = 0; j < kADma; ++j) {
     const int r = 8 * (4 * j + wv) + (lane >> 3);
-    const int gch = ((lane & 7) ^ (r & 7)) * 8;
+    const int gch = ((lane & 7) ^ lds_swizzle(r)) * 8;
     const int row = m0 + min(r, rows_here - 1);         // rows past the group repeat its last row
     if (GATE_UP) {
       const int tok = shared ? row : slot_tok[seg0 + row];
@@ -270,7 +277,7 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
     if constexpr (decltype(issue_c)::value) issue(wnext, (st + 3) % NS, ks + 3);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t sa = lds_base + st * kATile + l16 * 128 + (((2 * q + h) ^ (l16 & 7)) << 4);
+      const uint32_t sa = lds_base + st * kATile + l16 * 128 + (((2 * q + h) ^ lds_swizzle(l16)) << 4);
       u32x4 av[kGroup];
       lds_read_group<0>(av, sa, std::make_integer_sequence<int, kGroup>{});
       wait_lds(av);
