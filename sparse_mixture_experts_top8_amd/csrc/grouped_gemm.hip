@@ -52,6 +52,7 @@
 // side by side in one XCD and share them through its L2.
 #include "kernels.hpp"
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
                                                              const int4* __restrict__ tdesc,
                                                              const int* __restrict__ slot_tok,
                                                              const int* __restrict__ window,
-                                                             const int* __restrict__ slot_map) {
+                                                             const int* __restrict__ slot_map, int unit) {
   using S = TileShape<BM>;
   constexpr int kATile = S::kATile, kMBlocks = S::kMBlocks, kGroup = S::kGroup, kADma = S::kADma;
   constexpr int kVmPerStep = S::kVmPerStep;
@@ -158,10 +159,33 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
     ntiles = uni(prefix[E + 1]);
     n0 = ntiles;
   }
-  const int chunk = (ntiles + 7) >> 3;
-  const int j8 = blockIdx.x >> 3;
-  if (j8 >= chunk) return;
-  const int t = (blockIdx.x & 7) * chunk + j8;
+  // unit == 0: XCD x takes the x-th contiguous eighth of the tile list, in
+  // order.  Otherwise units of `unit` consecutive tiles (the workgroups one
+  // XCD holds at once) are dealt to the XCDs in turn, unit u to XCD u % 8, for as many
+  // whole rounds of eight units as the list holds; the rest is cut into eight
+  // equal parts, one per XCD.  Workgroup j of XCD x (blockIdx = 8 j + x) takes
+  // tile j % unit of unit (j / unit) * 8 + x in the whole rounds, so an XCD
+  // works through its units in order with each unit's tiles side by side, and
+  // every XCD gets a share of hot and cold groups alike and the same number
+  // of tiles, +-1 (with eight contiguous ranges, the range holding the hot
+  // experts' or the shared group's tiles ran on alone at the end: MI355X,
+  // Zipf(1.1) loads over 16384 tokens, one XCD for the last ~50 us of
+  // gate_up).  The grid holds at least one round more than the whole rounds,
+  // so every tile has its workgroup.
+  const int j8 = blockIdx.x >> 3, xcd = (int)(blockIdx.x & 7);
+  const int rounds = unit ? ntiles / (8 * unit) : 0, full = rounds * unit;
+  int t;
+  if (!unit) {
+    const int chunk = (ntiles + 7) >> 3;
+    if (j8 >= chunk) return;
+    t = xcd * chunk + j8;
+  } else if (j8 < full) {
+    t = ((j8 / unit) * 8 + xcd) * unit + j8 % unit;
+  } else {
+    const int rest = ntiles - 8 * full, part = (rest + 7) >> 3, jj = j8 - full;
+    if (jj >= part) return;
+    t = 8 * full + xcd * part + jj;
+  }
   if (t >= ntiles) return;
   const int4 d = tdesc[t < n0 ? lo0 + t : lo1 + (t - n0)];
   const int g = uni(d.x), seg0 = uni(d.y), nrows = uni(d.z);
@@ -423,7 +447,21 @@ __global__ __launch_bounds__(NT) void combine_kernel(int T, int H, int K, Work w
   __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (size_t)t * H + c));
 }
 
-unsigned gemm_grid(int64_t bound) { return (unsigned)(8 * ((bound + 7) / 8)); }
+// Tiles an XCD holds at once (workgroups per CU times its CUs), and the
+// grid: the whole rounds of eight units below the tile bound and one more
+// (unit 0, contiguous ranges: the bound rounded up to a multiple of eight).
+int gemm_unit(int per_cu, int num_cus) { return std::max(1, per_cu * (num_cus > 0 ? num_cus : 256) / 8); }
+unsigned gemm_grid(int64_t bound, int unit) {
+  if (!unit) return (unsigned)(8 * ((bound + 7) / 8));
+  const int64_t r = 8 * (int64_t)unit;
+  return (unsigned)(r * (bound / r + 1));
+}
+// Units dealt in turn for batches of at least two 160-row tiles per expert
+// on average, where expert loads may be skewed enough for contiguous ranges
+// to end unevenly (MI355X, Zipf(1.1) over 16384 tokens: gate_up 713 -> 660
+// us); contiguous ranges below (4096 tokens, 128 rows per expert, measured
+// 437 us per layer with contiguous ranges against 443 us with units).
+static bool gemm_units(const LayerArgs& L, int T) { return (int64_t)T * L.K >= 2 * (int64_t)L.E * kGemmBM; }
 
 }  // namespace
 
@@ -443,25 +481,33 @@ static auto gemm_kernel_for(const LayerArgs& L, int T) {
                               : grouped_gemm_kernel<GATE_UP, 0, kGemmBM>;
 }
 
+static int gemm_per_cu(const LayerArgs& L, int T) {
+  return gemm_small_rows(T, L.K, L.E) ? TileShape<kGemmBMSmall>::kPerCU : TileShape<kGemmBM>::kPerCU;
+}
+
 hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work& w, int num_cus,
                           hipStream_t s, const int* window, const int* slot_map) {
-  (void)num_cus;
   // The dispatch tables go in as separate read-only arguments: uniform reads of
   // them then compile to scalar loads.
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, 2 * L.I, 2 * L.Is);
+  const int unit = gemm_units(L, T) ? gemm_unit(gemm_per_cu(L, T), num_cus) : 0;
   auto k = gemm_kernel_for<true>(L, T);
-  hipLaunchKernelGGL(k, dim3(gemm_grid(bound)), dim3(256), 0, s, L, x, T, w, (const int*)w.tiles_gu,
-                     (const int4*)w.tdesc_gu, (const int*)w.slot_tok, window, slot_map);
+  hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(256), 0, s, L, x, T, w, (const int*)w.tiles_gu,
+                     (const int4*)w.tdesc_gu, (const int*)w.slot_tok, window, slot_map, unit);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s, const int* window,
                        const int* slot_map) {
-  (void)num_cus;
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, L.H, L.H);
+  // Each group has H / 128 down tiles per row tile against 2I / 128 gate_up
+  // tiles: units that many times larger deal every group to the XCD that ran
+  // its gate_up tiles, whose L2 may still hold its h rows.
+  const int ngu = (2 * L.I + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
+  const int unit = gemm_units(L, T) ? gemm_unit(gemm_per_cu(L, T), num_cus) * std::max(1, ndn / ngu) : 0;
   auto k = gemm_kernel_for<false>(L, T);
-  hipLaunchKernelGGL(k, dim3(gemm_grid(bound)), dim3(256), 0, s, L, (const bf16_t*)nullptr, T, w,
-                     (const int*)w.tiles_dn, (const int4*)w.tdesc_dn, (const int*)w.slot_tok, window, slot_map);
+  hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(256), 0, s, L, (const bf16_t*)nullptr, T, w,
+                     (const int*)w.tiles_dn, (const int4*)w.tdesc_dn, (const int*)w.slot_tok, window, slot_map, unit);
   return hipGetLastError();
 }
 
