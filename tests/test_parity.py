@@ -293,10 +293,12 @@ def test_full_workloads(full, name):
     check_output(xb, lb, d, gi, _np(out.float()), np.arange(wl.T), name)
 
 
-@pytest.mark.parametrize("T", [2049, 6000])
+@pytest.mark.parametrize("T", [2049, 6000, 12000])
 def test_full_past_dispatch_switch(full, T):
-    # Full shape just past the one-workgroup dispatch (2048 tokens) and at
-    # ~190 rows per expert (two 160-row tiles for most experts), whole output.
+    # Full shape just past the one-workgroup dispatch (2048 tokens), at ~190
+    # rows per expert (two 160-row tiles for most experts), and at ~375 rows
+    # per expert, where the GEMM tiles go to the XCDs in units dealt in turn
+    # (uniform loads: a partial last round of units), whole output.
     d, bits, layer, _, _ = full
     _say(f"case full past the dispatch switch T={T}")
     xb = mi.make_x(d, T, 9950 + T)
