@@ -58,18 +58,19 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
   __shared__ int wave_tot[4];
   const int e = threadIdx.x;
   const int E = L.E, K = L.K;
-  const int bm = gemm_bm(T, K, E);
+  const int bmg = gemm_bm(T, K, E, true), bng = gemm_bn(T, K, E, true);
+  const int bmd = gemm_bm(T, K, E, false), bnd = gemm_bn(T, K, E, false);
   const int cnt = e < E ? w.offsets[e] : 0;
   const int incl = block_inclusive_scan(cnt, wave_tot);
   if (e < E) w.offsets[e] = incl - cnt;
   if (e == 0) w.offsets[E] = T * K;
 
-  // Tiles per group: ceil(rows / bm) row tiles x (weight rows / BNW) column tiles.
+  // Tiles per group: ceil(rows / bm) row tiles x (weight rows / bn) column
+  // tiles, each GEMM with its own tile shape (gemm_bm, gemm_bn).
   int gu = 0, dn = 0;
   if (e < E) {
-    int mt = (cnt + bm - 1) / bm;
-    gu = mt * ((2 * L.I + kGemmBNW - 1) / kGemmBNW);
-    dn = mt * (L.H / kGemmBNW);
+    gu = ((cnt + bmg - 1) / bmg) * ((2 * L.I + bng - 1) / bng);
+    dn = ((cnt + bmd - 1) / bmd) * (L.H / bnd);
   }
   const int gu_incl = block_inclusive_scan(gu, wave_tot);
   const int dn_incl = block_inclusive_scan(dn, wave_tot);
@@ -78,11 +79,10 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
     w.tiles_dn[e] = dn_incl - dn;
   }
   if (e == E - 1) {
-    const int mt = (T + bm - 1) / bm;
     w.tiles_gu[E] = gu_incl;
     w.tiles_dn[E] = dn_incl;
-    w.tiles_gu[E + 1] = gu_incl + mt * ((2 * L.Is + kGemmBNW - 1) / kGemmBNW);
-    w.tiles_dn[E + 1] = dn_incl + mt * (L.H / kGemmBNW);
+    w.tiles_gu[E + 1] = gu_incl + ((T + bmg - 1) / bmg) * ((2 * L.Is + bng - 1) / bng);
+    w.tiles_dn[E + 1] = dn_incl + ((T + bmd - 1) / bmd) * (L.H / bnd);
   }
 }
 
@@ -90,21 +90,22 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
 // its tiles in both grouped GEMMs, in gemm_tile_order.
 __device__ void dispatch_tiles(LayerArgs L, int T, const Work& w, int g) {
   const int E = L.E;
-  const int bm = gemm_bm(T, L.K, E);
+  const int bmg = gemm_bm(T, L.K, E, true), bng = gemm_bn(T, L.K, E, true);
+  const int bmd = gemm_bm(T, L.K, E, false), bnd = gemm_bn(T, L.K, E, false);
   const bool shared = g == E;
   const int seg0 = shared ? 0 : w.offsets[g];
   const int nrows = shared ? T : w.offsets[g + 1] - seg0;
-  const int mt = (nrows + bm - 1) / bm;
-  const int ngu = (2 * (shared ? L.Is : L.I) + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
+  const int mtg = (nrows + bmg - 1) / bmg, mtd = (nrows + bmd - 1) / bmd;
+  const int ngu = (2 * (shared ? L.Is : L.I) + bng - 1) / bng, ndn = L.H / bnd;
   const int bgu = w.tiles_gu[g], bdn = w.tiles_dn[g];
-  for (int i = threadIdx.x; i < mt * ngu; i += 256) {
+  for (int i = threadIdx.x; i < mtg * ngu; i += 256) {
     int mi, nt;
-    gemm_tile_order(i, mt, ngu, mi, nt);
+    gemm_tile_order(i, mtg, ngu, mi, nt);
     w.tdesc_gu[bgu + i] = make_int4(g, seg0, nrows, mi | (nt << 16));
   }
-  for (int i = threadIdx.x; i < mt * ndn; i += 256) {
+  for (int i = threadIdx.x; i < mtd * ndn; i += 256) {
     int mi, nt;
-    gemm_tile_order(i, mt, ndn, mi, nt);
+    gemm_tile_order(i, mtd, ndn, mi, nt);
     w.tdesc_dn[bdn + i] = make_int4(g, seg0, nrows, mi | (nt << 16));
   }
 }
@@ -154,7 +155,8 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
   __shared__ int wave_tot[kSmallThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = L.E, K = L.K, TK = T * K;
-  const int bm = gemm_bm(T, K, E);
+  const int bmg = gemm_bm(T, K, E, true), bng = gemm_bn(T, K, E, true);
+  const int bmd = gemm_bm(T, K, E, false), bnd = gemm_bn(T, K, E, false);
   const int nblk = router_blocks(T);
   for (int i = tid; i < nblk * E; i += kSmallThreads) s_mask[i] = 0u;
   __syncthreads();
@@ -181,8 +183,9 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
       const int cnt = e < E ? s_cnt[e] : 0;
-      const int mt = (cnt + bm - 1) / bm;
-      v[j] = wave == 0 ? cnt : (wave == 1 ? mt * ((2 * L.I + kGemmBNW - 1) / kGemmBNW) : mt * (L.H / kGemmBNW));
+      v[j] = wave == 0 ? cnt
+                       : (wave == 1 ? ((cnt + bmg - 1) / bmg) * ((2 * L.I + bng - 1) / bng)
+                                    : ((cnt + bmd - 1) / bmd) * (L.H / bnd));
       run += v[j];
     }
     int incl = run;
@@ -200,10 +203,9 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
       ex += v[j];
     }
     if (lane == 63) {
-      const int mt = (T + bm - 1) / bm;
       dst[E] = incl;
-      if (wave == 1) dst[E + 1] = incl + mt * ((2 * L.Is + kGemmBNW - 1) / kGemmBNW);
-      if (wave == 2) dst[E + 1] = incl + mt * (L.H / kGemmBNW);
+      if (wave == 1) dst[E + 1] = incl + ((T + bmg - 1) / bmg) * ((2 * L.Is + bng - 1) / bng);
+      if (wave == 2) dst[E + 1] = incl + ((T + bmd - 1) / bmd) * (L.H / bnd);
     }
   }
   __syncthreads();
@@ -219,8 +221,8 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
   // nt * rows + row.  (Small batches give the shared group many row tiles,
   // so one thread per group would be a long serial path.)
   {
-    const int ngu_r = (2 * L.I + kGemmBNW - 1) / kGemmBNW, ngu_s = (2 * L.Is + kGemmBNW - 1) / kGemmBNW;
-    const int ndn = L.H / kGemmBNW, gumax = max(ngu_r, ngu_s), ncols = gumax + ndn;
+    const int ngu_r = (2 * L.I + bng - 1) / bng, ngu_s = (2 * L.Is + bng - 1) / bng;
+    const int ndn = L.H / bnd, gumax = max(ngu_r, ngu_s), ncols = gumax + ndn;
     for (int c = wave; c < ncols; c += kSmallThreads / 64) {
       for (int g = lane; g <= E; g += 64) {
         const bool shared = g == E, gu = c < gumax;
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
         if (nt >= ncol) continue;
         const int seg0 = shared ? 0 : s_off[g];
         const int nrows = shared ? T : s_cnt[g];
-        const int mt = (nrows + bm - 1) / bm;
+        const int bm = gu ? bmg : bmd, mt = (nrows + bm - 1) / bm;
         int4* base = gu ? w.tdesc_gu + s_tgu[g] : w.tdesc_dn + s_tdn[g];
         for (int b0 = 0; b0 < mt; b0 += kGemmRowBlock) {
           const int rows = min(kGemmRowBlock, mt - b0);

@@ -60,19 +60,23 @@ namespace moe {
 
 namespace {
 
-constexpr int BN = kGemmBNW;     // 128 weight rows
 constexpr int BK = 64;
 constexpr int NS = 4;            // ring depth (activation LDS stages = weight register slots)
-// Shape of a tile of BM rows (160, or 32 for small batches).
-template <int BM>
+// Shape of a tile of BM rows and NW waves, each wave owning 32 weight rows
+// (160 x 128 with four waves; 32 x 128 for small batches; 192 x 256 with
+// eight waves for large ones).
+template <int BM, int NW>
 struct TileShape {
-  static constexpr int kATile = BM * BK * 2;        // activation stage: 20 KB (160 rows), 4 KB (32 rows)
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kBN = 32 * NW;                // weight rows per tile
+  static constexpr int kATile = BM * BK * 2;        // activation stage: 20 KB (160 rows), 4 KB (32), 24 KB (192)
   static constexpr int kMBlocks = BM / 16;          // 16-row MFMA blocks
-  static constexpr int kGroup = kMBlocks < 5 ? kMBlocks : 5;   // blocks read from LDS together
-  static constexpr int kADma = BM * 8 / 256;        // direct-to-LDS instructions per wave per step (16-byte units / 256 threads)
+  static constexpr int kGroup = kMBlocks <= 6 ? kMBlocks : kMBlocks / 2;   // blocks read from LDS together
+  static constexpr int kADma = BM * 8 / kThreads;   // direct-to-LDS instructions per wave per step (16-byte units / threads)
   static constexpr int kVmPerStep = kADma + 4;      // per wave: activation loads + 4 weight loads
-  static constexpr int kPerCU = BM > 64 ? 2 : 4;    // workgroups per CU (LDS: NS stages each)
-  static_assert((BM * 8) % 256 == 0 && (kMBlocks == kGroup || kMBlocks == 2 * kGroup),
+  static constexpr int kPerCU = NW == 8 ? 1 : (BM > 64 ? 2 : 4);   // workgroups per CU (LDS: NS stages each)
+  static constexpr int kLds = NS * kATile > NW * BM * 64 ? NS * kATile : NW * BM * 64;   // ring, or the epilogue tiles
+  static_assert((BM * 8) % kThreads == 0 && (kMBlocks == kGroup || kMBlocks == 2 * kGroup),
                 "rows are read in one or two groups of blocks");
 };
 
@@ -91,7 +95,7 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
   return v;
 }
-// Operands of five consecutive 16-row blocks I0 .. I0 + 4: one base address
+// Operands of G consecutive 16-row blocks I0 .. I0 + G - 1: one base address
 // per lane, the blocks 2048 bytes apart (16 rows of 128 bytes; the chunk
 // swizzle depends on row % 8 only, which is the same in every block).
 template <int I0, int G, int... I>
@@ -105,6 +109,9 @@ __device__ __forceinline__ void wait_lds(u32x4 (&a)[5]) {
 }
 __device__ __forceinline__ void wait_lds(u32x4 (&a)[2]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]) : : "memory");
+}
+__device__ __forceinline__ void wait_lds(u32x4 (&a)[6]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]) : : "memory");
 }
 // s_waitcnt vmcnt(N) through the builtin, which the compiler's own wait
 // insertion takes into account (it cannot see inside inline asm, and would
@@ -131,18 +138,20 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 // WAUX: cache policy of the weight loads (0, or kNonTemporal for batches so
 // small that each weight fragment feeds one tile of a few rows).  BM: rows
-// per tile.
-template <bool GATE_UP, int WAUX, int BM>
-__global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
+// per tile; NW: waves (4, or 8 for the 192 x 256 tiles of large batches,
+// which read 56 KB per k-step for 192 x 256 outputs where two 160 x 128
+// workgroups read 72 KB for 2 x 160 x 128).
+template <bool GATE_UP, int WAUX, int BM, int NW>
+__global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::kPerCU)) void grouped_gemm_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
                                                              Work w, const int* __restrict__ prefix,
                                                              const int4* __restrict__ tdesc,
                                                              const int* __restrict__ slot_tok,
                                                              const int* __restrict__ window,
                                                              const int* __restrict__ slot_map, int unit) {
-  using S = TileShape<BM>;
+  using S = TileShape<BM, NW>;
   constexpr int kATile = S::kATile, kMBlocks = S::kMBlocks, kGroup = S::kGroup, kADma = S::kADma;
-  constexpr int kVmPerStep = S::kVmPerStep;
-  __shared__ __attribute__((aligned(1024))) char lds[NS * kATile];
+  constexpr int kVmPerStep = S::kVmPerStep, BN = S::kBN;
+  __shared__ __attribute__((aligned(1024))) char lds[S::kLds];
 
   const int E = L.E, K = L.K, H = L.H;
   // Tile of this workgroup: XCD x = blockIdx % 8 takes the x-th contiguous
@@ -206,13 +215,13 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
   const uint32_t lds_base = (uint32_t)(size_t)(lds_ptr_t)lds;
 
   // ---- activation sources: direct-to-LDS instruction j (0..kADma-1) of
-  // wave w writes 16-byte unit p = 64 (4 j + w) + lane, i.e. row
-  // r = 8 (4 j + w) + lane / 8, stored chunk lane % 8, holding the global
+  // wave w writes 16-byte unit p = 64 (NW j + w) + lane, i.e. row
+  // r = 8 (NW j + w) + lane / 8, stored chunk lane % 8, holding the global
   // chunk (lane % 8) ^ swz(r).
   const bf16_t* a_src[kADma];
 #pragma unroll
   for (int j = 0; j < kADma; ++j) {
-    const int r = 8 * (4 * j + wv) + (lane >> 3);
+    const int r = 8 * (NW * j + wv) + (lane >> 3);
     const int gch = ((lane & 7) ^ lds_swizzle(r)) * 8;
     const int row = m0 + min(r, rows_here - 1);         // rows past the group repeat its last row
     if (GATE_UP) {
@@ -236,15 +245,15 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
     const int nk = kdim / BK;
     if (GATE_UP) {
       b_rs[0] = b_rs[1] = make_rsrc(L.gate_up_w + (size_t)gw * 2 * L.I * H, (uint32_t)(2 * L.I * H * 2));
-      b_off[0] = 2048u * (uint32_t)((nt * 4 + wv) * nk) + 16u * lane;
-      b_off[1] = 2048u * (uint32_t)((L.I / 16 + nt * 4 + wv) * nk) + 16u * lane;
+      b_off[0] = 2048u * (uint32_t)((nt * NW + wv) * nk) + 16u * lane;
+      b_off[1] = 2048u * (uint32_t)((L.I / 16 + nt * NW + wv) * nk) + 16u * lane;
     } else {
       b_rs[0] = b_rs[1] = make_rsrc(L.down_w + (size_t)gw * H * L.I, (uint32_t)(H * kdim * 2));
 #pragma unroll
-      for (int b = 0; b < 2; ++b) b_off[b] = 2048u * (uint32_t)((nt * 8 + 2 * wv + b) * nk) + 16u * lane;
+      for (int b = 0; b < 2; ++b) b_off[b] = 2048u * (uint32_t)((nt * 2 * NW + 2 * wv + b) * nk) + 16u * lane;
     }
   } else if (GATE_UP) {
-    const int inner = min(nt * 64 + 16 * wv + l16, inner_n - 1);   // past the inner size: repeated, dropped
+    const int inner = min(nt * 16 * NW + 16 * wv + l16, inner_n - 1);   // past the inner size: repeated, dropped
     if (shared) {
       b_rs[0] = make_rsrc(L.sh_gate_w, (uint32_t)(L.Is * H * 2));
       b_rs[1] = make_rsrc(L.sh_up_w, (uint32_t)(L.Is * H * 2));
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
     const int kv = min(ks, nreal - 1);          // padding steps re-read the last real step
 #pragma unroll
     for (int j = 0; j < kADma; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + kv * BK), (lds_ptr_t)(sbase + 1024 * (4 * j + wv)),
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + kv * BK), (lds_ptr_t)(sbase + 1024 * (NW * j + wv)),
                                        16, 0, 0);
     const bool real = ks < nreal;
 #pragma unroll
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
   // resource and are dropped.
   barrier();
   bf16_t* ep = reinterpret_cast<bf16_t*>(lds + wv * (BM * 32 * 2));    // BM rows x 32 columns per wave
-  static_assert(4 * BM * 32 * 2 <= NS * kATile, "the epilogue tiles fit in the ring");
+  static_assert(NW * BM * 32 * 2 <= S::kLds, "the epilogue tiles fit in LDS");
   constexpr int kCols = GATE_UP ? 16 : 32;
 #pragma unroll
   for (int i = 0; i < kMBlocks; ++i)
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(256, TileShape<BM>::kPerCU) void grouped_gemm_kerne
   uint32_t ostride, ocol;
   bool wave_ok = true;
   if (GATE_UP) {
-    ocol = nt * 64 + 16 * wv;
+    ocol = nt * 16 * NW + 16 * wv;
     wave_ok = (int)ocol < inner_n;
     ostride = inner_n * 2;
     obase = (shared ? w.h_sh : w.h) + (size_t)(seg0 + m0) * inner_n;
@@ -457,11 +466,12 @@ unsigned gemm_grid(int64_t bound, int unit) {
   return (unsigned)(r * (bound / r + 1));
 }
 // Units dealt in turn for batches of at least two 160-row tiles per expert
-// on average, where expert loads may be skewed enough for contiguous ranges
-// to end unevenly (MI355X, Zipf(1.1) over 16384 tokens: gate_up 713 -> 660
-// us); contiguous ranges below (4096 tokens, 128 rows per expert, measured
-// 437 us per layer with contiguous ranges against 443 us with units).
-static bool gemm_units(const LayerArgs& L, int T) { return (int64_t)T * L.K >= 2 * (int64_t)L.E * kGemmBM; }
+// on average (gemm_wide), where expert loads may be skewed enough for
+// contiguous ranges to end unevenly (MI355X, Zipf(1.1) over 16384 tokens:
+// gate_up 713 -> 660 us); contiguous ranges below (4096 tokens, 128 rows per
+// expert, measured 437 us per layer with contiguous ranges against 443 us
+// with units).
+static bool gemm_units(const LayerArgs& L, int T) { return gemm_wide(T, L.K, L.E); }
 
 }  // namespace
 
@@ -472,27 +482,34 @@ static bool gemm_units(const LayerArgs& L, int T) { return (int64_t)T * L.K >= 2
 // zipf16384 +19 %, where hot experts' weights are reused across row tiles).
 static bool stream_weights(const LayerArgs& L, int T) { return (int64_t)T * L.K <= 16 * (int64_t)L.E; }
 
-// Kernel of a batch: 32-row tiles for the smallest batches (gemm_bm), weight
-// cache policy by stream_weights.
+// Kernel of a batch: the tile shape by gemm_bm / gemm_bn (32 x 128 for the
+// smallest batches, 192 x 256 with eight waves for the largest, else
+// 160 x 128), weight cache policy by stream_weights.
 template <bool GATE_UP>
 static auto gemm_kernel_for(const LayerArgs& L, int T) {
-  if (gemm_small_rows(T, L.K, L.E)) return grouped_gemm_kernel<GATE_UP, kNonTemporal, kGemmBMSmall>;
-  return stream_weights(L, T) ? grouped_gemm_kernel<GATE_UP, kNonTemporal, kGemmBM>
-                              : grouped_gemm_kernel<GATE_UP, 0, kGemmBM>;
+  if (gemm_small_rows(T, L.K, L.E)) return grouped_gemm_kernel<GATE_UP, kNonTemporal, kGemmBMSmall, 4>;
+  if (GATE_UP && gemm_wide(T, L.K, L.E)) return grouped_gemm_kernel<GATE_UP, 0, kGemmBMWide, 8>;
+  return stream_weights(L, T) ? grouped_gemm_kernel<GATE_UP, kNonTemporal, kGemmBM, 4>
+                              : grouped_gemm_kernel<GATE_UP, 0, kGemmBM, 4>;
 }
+static_assert(TileShape<kGemmBMWide, 8>::kBN == kGemmBNWide && TileShape<kGemmBM, 4>::kBN == kGemmBNW &&
+                  TileShape<kGemmBMSmall, 4>::kBN == kGemmBNW,
+              "the dispatch's column tiles match the kernels'");
 
-static int gemm_per_cu(const LayerArgs& L, int T) {
-  return gemm_small_rows(T, L.K, L.E) ? TileShape<kGemmBMSmall>::kPerCU : TileShape<kGemmBM>::kPerCU;
+static int gemm_per_cu(const LayerArgs& L, int T, bool gate_up) {
+  if (gemm_small_rows(T, L.K, L.E)) return TileShape<kGemmBMSmall, 4>::kPerCU;
+  return gate_up && gemm_wide(T, L.K, L.E) ? TileShape<kGemmBMWide, 8>::kPerCU : TileShape<kGemmBM, 4>::kPerCU;
 }
+static int gemm_threads(const LayerArgs& L, int T, bool gate_up) { return gate_up && gemm_wide(T, L.K, L.E) ? 512 : 256; }
 
 hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work& w, int num_cus,
                           hipStream_t s, const int* window, const int* slot_map) {
   // The dispatch tables go in as separate read-only arguments: uniform reads of
   // them then compile to scalar loads.
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, 2 * L.I, 2 * L.Is);
-  const int unit = gemm_units(L, T) ? gemm_unit(gemm_per_cu(L, T), num_cus) : 0;
+  const int unit = gemm_units(L, T) ? gemm_unit(gemm_per_cu(L, T, true), num_cus) : 0;
   auto k = gemm_kernel_for<true>(L, T);
-  hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(256), 0, s, L, x, T, w, (const int*)w.tiles_gu,
+  hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(gemm_threads(L, T, true)), 0, s, L, x, T, w, (const int*)w.tiles_gu,
                      (const int4*)w.tdesc_gu, (const int*)w.slot_tok, window, slot_map, unit);
   return hipGetLastError();
 }
@@ -500,13 +517,19 @@ hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work
 hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hipStream_t s, const int* window,
                        const int* slot_map) {
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, L.H, L.H);
-  // Each group has H / 128 down tiles per row tile against 2I / 128 gate_up
-  // tiles: units that many times larger deal every group to the XCD that ran
+  // Units in the ratio of a group's down tiles to its gate_up tiles (row and
+  // column tiles of either shape) deal every group to about the XCD that ran
   // its gate_up tiles, whose L2 may still hold its h rows.
-  const int ngu = (2 * L.I + kGemmBNW - 1) / kGemmBNW, ndn = L.H / kGemmBNW;
-  const int unit = gemm_units(L, T) ? gemm_unit(gemm_per_cu(L, T), num_cus) * std::max(1, ndn / ngu) : 0;
+  int unit = 0;
+  if (gemm_units(L, T)) {
+    const int bmg = gemm_bm(T, L.K, L.E, true), bng = gemm_bn(T, L.K, L.E, true);
+    const int bmd = gemm_bm(T, L.K, L.E, false), bnd = gemm_bn(T, L.K, L.E, false);
+    const int64_t ngu = (2 * L.I + bng - 1) / bng, ndn = L.H / bnd;
+    const int64_t ug = gemm_unit(gemm_per_cu(L, T, true), num_cus);
+    unit = (int)std::max<int64_t>(1, ug * ndn * bmg / (ngu * bmd));
+  }
   auto k = gemm_kernel_for<false>(L, T);
-  hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(256), 0, s, L, (const bf16_t*)nullptr, T, w,
+  hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(gemm_threads(L, T, false)), 0, s, L, (const bf16_t*)nullptr, T, w,
                      (const int*)w.tiles_dn, (const int4*)w.tdesc_dn, (const int*)w.slot_tok, window, slot_map, unit);
   return hipGetLastError();
 }

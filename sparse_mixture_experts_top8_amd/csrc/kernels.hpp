@@ -18,12 +18,23 @@ constexpr int kRouterTokens = 32;
 constexpr int kGemmBM = 160;
 constexpr int kGemmBMSmall = 32;
 constexpr int kGemmBNW = 128;   // weight rows per tile: gate_up 64 gate + 64 up; down 128 H cols
+// Large batches: gate_up in 192-row tiles of 256 weight rows (eight waves
+// per workgroup); the down projection keeps 160 x 128.
+constexpr int kGemmBMWide = 192;
+constexpr int kGemmBNWide = 256;
 __host__ __device__ inline bool gemm_small_rows(int64_t T, int K, int E) { return T * K <= 8 * (int64_t)E; }
-__host__ __device__ inline int gemm_bm(int64_t T, int K, int E) {
-  return gemm_small_rows(T, K, E) ? kGemmBMSmall : kGemmBM;
+// From two 160-row tiles per expert on average.
+__host__ __device__ inline bool gemm_wide(int64_t T, int K, int E) { return T * K >= 2 * (int64_t)E * kGemmBM; }
+// Rows and weight rows per tile of either GEMM.
+__host__ __device__ inline int gemm_bm(int64_t T, int K, int E, bool gate_up) {
+  return gemm_small_rows(T, K, E) ? kGemmBMSmall : (gate_up && gemm_wide(T, K, E) ? kGemmBMWide : kGemmBM);
+}
+__host__ __device__ inline int gemm_bn(int64_t T, int K, int E, bool gate_up) {
+  return gate_up && gemm_wide(T, K, E) ? kGemmBNWide : kGemmBNW;
 }
 // Upper bound of the tiles of one grouped GEMM (workspace and grid size):
-// every group adds at most one partial row tile.  Past the switch to 160-row
+// every group adds at most one partial row tile.  Counted with 160 x 128
+// tiles, it also bounds the fewer 192 x 256 tiles of large batches.  Past the switch to 160-row
 // tiles the bound keeps the 32-row bound of the largest small batch, so it
 // never decreases as T grows (a workspace sized for T serves smaller batches).
 __host__ __device__ inline int64_t gemm_tile_bound_bm(int64_t T, int K, int E, int wrows, int wrows_shared, int bm) {
