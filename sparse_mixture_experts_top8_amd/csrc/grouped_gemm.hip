@@ -16,7 +16,9 @@
 // typical expert of a 4096-token batch, about 128 +- 11 rows, in one tile, so
 // its weights stream once); two workgroups share a CU, so one's start-up
 // overlaps the other's streaming.  Batches of a few rows per expert use
-// 32-row tiles, four workgroups per CU.  Wave w owns weight
+// 32-row tiles, four workgroups per CU; batches of many (two 160-row tiles
+// per expert on average) run gate_up in 192 x 256 tiles of eight waves, one
+// workgroup per CU (the down projection keeps 160 x 128).  Wave w owns weight
 // rows 32w .. 32w + 31 of the tile as two 16-column MFMA blocks: for gate_up
 // the gate rows and the up rows of the same 16 inner rows (SiLU(g) * u is
 // formed in registers, both blocks having the same layout), for down 32 output
@@ -25,7 +27,7 @@
 // k advances in steps of 64 through a four-deep ring, three steps in flight:
 // the weight fragments of a wave are needed by that wave alone and go straight
 // into registers in MFMA operand layout; the activation tile (gathered x rows
-// or h rows) is shared by the four waves and goes to LDS by the direct-to-LDS
+// or h rows) is shared by the tile's waves and goes to LDS by the direct-to-LDS
 // loads (global_load_lds_dwordx4).  Within a k-step, lane quarter q (lane / 16)
 // covers k 16q .. 16q + 15, eight per MFMA k-step; activations and weights
 // use the same order, so the products are unchanged and each lane reads 32
@@ -46,7 +48,8 @@
 //
 // Scheduling: workgroups are handed to the eight XCDs round-robin (workgroup i
 // on XCD i % 8); the tile list is cut into eight contiguous ranges and XCD x
-// takes range x in order.  Within a group, tiles come in blocks of eight row
+// takes range x in order, or for large batches dealt to the XCDs in units
+// (see the kernel).  Within a group, tiles come in blocks of eight row
 // tiles, column tile major inside a block (gemm_tile_order): a block's row
 // tiles of one weight slab, and its column tiles of one activation block, run
 // side by side in one XCD and share them through its L2.
@@ -319,7 +322,7 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
         acc[i][0] = mfma16(av[i], wcur[0][h], acc[i][0]);
         acc[i][1] = mfma16(av[i], wcur[1][h], acc[i][1]);
       }
-      // A second group of 16-row blocks (160-row tiles) is skipped when the
+      // A second group of 16-row blocks (160- and 192-row tiles) is skipped when the
       // tile's rows end before it (uniform branch).
       if constexpr (kMBlocks > kGroup) {
         if (mblocks > kGroup) {
