@@ -105,16 +105,21 @@ template <int I0, int G, int... I>
 __device__ __forceinline__ void lds_read_group(u32x4 (&a)[G], uint32_t addr, std::integer_sequence<int, I...>) {
   ((a[I] = lds_read16<2048 * (I0 + I)>(addr)), ...);
 }
-// Waits for the LDS reads and ties their result registers to the wait, so
-// that no use of them can be scheduled before it.
-__device__ __forceinline__ void wait_lds(u32x4 (&a)[5]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]) : : "memory");
+// Waits until at most N LDS reads are outstanding and ties the group's
+// registers to the wait, so that no use of them can be scheduled before it
+// (the group is older than the last N reads).
+template <int N>
+__device__ __forceinline__ void wait_lds_keep(u32x4 (&a)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a[0]), "+v"(a[1]) : "n"(N) : "memory");
 }
-__device__ __forceinline__ void wait_lds(u32x4 (&a)[2]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]) : : "memory");
+template <int N>
+__device__ __forceinline__ void wait_lds_keep(u32x4 (&a)[5]) {
+  asm volatile("s_waitcnt lgkmcnt(%5)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]) : "n"(N) : "memory");
 }
-__device__ __forceinline__ void wait_lds(u32x4 (&a)[6]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]) : : "memory");
+template <int N>
+__device__ __forceinline__ void wait_lds_keep(u32x4 (&a)[6]) {
+  asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]) : "n"(N)
+               : "memory");
 }
 // s_waitcnt vmcnt(N) through the builtin, which the compiler's own wait
 // insertion takes into account (it cannot see inside inline asm, and would
@@ -311,30 +316,43 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
     wait_vm<YOUNGER * kVmPerStep>();   // this step's loads have landed
     barrier();   // every wave's part of the stage is in LDS; the stage read last step is free
     if constexpr (decltype(issue_c)::value) issue(wnext, (st + 3) % NS, ks + 3);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t sa = lds_base + st * kATile + l16 * 128 + (((2 * q + h) ^ lds_swizzle(l16)) << 4);
-      u32x4 av[kGroup];
-      lds_read_group<0>(av, sa, std::make_integer_sequence<int, kGroup>{});
-      wait_lds(av);
+    const uint32_t sa0 = lds_base + st * kATile + l16 * 128 + (((2 * q) ^ lds_swizzle(l16)) << 4);
+    const uint32_t sa1 = lds_base + st * kATile + l16 * 128 + (((2 * q + 1) ^ lds_swizzle(l16)) << 4);
+    using seq = std::make_integer_sequence<int, kGroup>;
+    auto mma = [&](int i0, int h, u32x4 (&av)[kGroup]) {
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
-        acc[i][0] = mfma16(av[i], wcur[0][h], acc[i][0]);
-        acc[i][1] = mfma16(av[i], wcur[1][h], acc[i][1]);
+        acc[i0 + i][0] = mfma16(av[i], wcur[0][h], acc[i0 + i][0]);
+        acc[i0 + i][1] = mfma16(av[i], wcur[1][h], acc[i0 + i][1]);
       }
-      // A second group of 16-row blocks (160- and 192-row tiles) is skipped when the
-      // tile's rows end before it (uniform branch).
-      if constexpr (kMBlocks > kGroup) {
-        if (mblocks > kGroup) {
-          lds_read_group<kGroup>(av, sa, std::make_integer_sequence<int, kGroup>{});
-          wait_lds(av);
-#pragma unroll
-          for (int i = 0; i < kGroup; ++i) {
-            acc[kGroup + i][0] = mfma16(av[i], wcur[0][h], acc[kGroup + i][0]);
-            acc[kGroup + i][1] = mfma16(av[i], wcur[1][h], acc[kGroup + i][1]);
-          }
-        }
-      }
+    };
+    // The operand groups of the step (k half 0, then 1; with two groups of
+    // 16-row blocks, rows of the first group, then the second) are read one
+    // group ahead of their MFMAs, so that the two waves of a SIMD, which
+    // leave the barrier together, do not wait for LDS at the same time.  The
+    // second group's MFMAs are skipped when the tile's rows end before it
+    // (uniform branch); its reads are not.
+    u32x4 X[kGroup], Y[kGroup];
+    if constexpr (kMBlocks > kGroup) {
+      lds_read_group<0>(X, sa0, seq{});
+      lds_read_group<kGroup>(Y, sa0, seq{});
+      wait_lds_keep<kGroup>(X);
+      mma(0, 0, X);
+      lds_read_group<0>(X, sa1, seq{});
+      wait_lds_keep<kGroup>(Y);
+      if (mblocks > kGroup) mma(kGroup, 0, Y);
+      lds_read_group<kGroup>(Y, sa1, seq{});
+      wait_lds_keep<kGroup>(X);
+      mma(0, 1, X);
+      wait_lds_keep<0>(Y);
+      if (mblocks > kGroup) mma(kGroup, 1, Y);
+    } else {
+      lds_read_group<0>(X, sa0, seq{});
+      lds_read_group<0>(Y, sa1, seq{});
+      wait_lds_keep<kGroup>(X);
+      mma(0, 0, X);
+      wait_lds_keep<0>(Y);
+      mma(0, 1, Y);
     }
   };
   static_assert(NS == 4, "the loop below is unrolled for four slots");
