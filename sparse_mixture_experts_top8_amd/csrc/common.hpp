@@ -190,6 +190,7 @@ struct Work {
   int32_t* offsets;    // [E + 1]
   int32_t* tiles_gu;   // [E + 2]   prefix of gate_up tiles per group (group E = shared)
   int32_t* tiles_dn;   // [E + 2]   prefix of down tiles per group
+  int32_t* claims;     // [2][8][32] persistent GEMMs' claim counters (gate_up, down), one per XCD, 128 bytes apart
   int4* tdesc_gu;      // per gate_up tile: group, first slot, rows, row tile | column tile << 16
   int4* tdesc_dn;      // per down tile, same
   int32_t* perm;       // [T*K]

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(LayerArgs L, int T, 
     w.tiles_gu[e] = gu_incl - gu;
     w.tiles_dn[e] = dn_incl - dn;
   }
+  if (e < 16) w.claims[32 * e] = 0;   // claim counters of the persistent GEMMs
   if (e == E - 1) {
     w.tiles_gu[E] = gu_incl;
     w.tiles_dn[E] = dn_incl;
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
     w.tiles_gu[g] = s_tgu[g];
     w.tiles_dn[g] = s_tdn[g];
   }
+  if (tid < 16) w.claims[32 * tid] = 0;   // claim counters of the persistent GEMMs
   // Tile descriptors in gemm_tile_order, one item per (group, column tile)
   // of either GEMM, waves over column tiles and lanes over groups.  Item
   // (g, nt) writes column tile nt of every row block of group g: a block of

@@ -149,7 +149,7 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // per tile; NW: waves (4, or 8 for the 192 x 256 tiles of large batches,
 // which read 56 KB per k-step for 192 x 256 outputs where two 160 x 128
 // workgroups read 72 KB for 2 x 160 x 128).
-template <bool GATE_UP, int WAUX, int BM, int NW>
+template <bool GATE_UP, int WAUX, int BM, int NW, bool PERSIST = false>
 __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::kPerCU)) void grouped_gemm_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
                                                              Work w, const int* __restrict__ prefix,
                                                              const int4* __restrict__ tdesc,
@@ -189,27 +189,49 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
   // Zipf(1.1) loads over 16384 tokens, one XCD for the last ~50 us of
   // gate_up).  The grid holds at least one round more than the whole rounds,
   // so every tile has its workgroup.
+  //
+  // PERSIST: one workgroup per CU instead, each taking the tiles its XCD would
+  // have run, in the same order, through a per-XCD counter (j = the number of
+  // tiles that XCD's workgroups took before); the next claim is requested at
+  // the start of each tile.  With one eight-wave workgroup per CU a new
+  // workgroup started ~2.2 us after the last one ended, plus ~0.8 us for the
+  // tile count and descriptor (MI355X, Zipf(1.1) over 16384 tokens, ~14 tiles
+  // per CU).
   const int j8 = blockIdx.x >> 3, xcd = (int)(blockIdx.x & 7);
   const int rounds = unit ? ntiles / (8 * unit) : 0, full = rounds * unit;
-  int t;
-  if (!unit) {
-    const int chunk = (ntiles + 7) >> 3;
-    if (j8 >= chunk) return;
-    t = xcd * chunk + j8;
-  } else if (j8 < full) {
-    t = ((j8 / unit) * 8 + xcd) * unit + j8 % unit;
-  } else {
-    const int rest = ntiles - 8 * full, part = (rest + 7) >> 3, jj = j8 - full;
-    if (jj >= part) return;
-    t = 8 * full + xcd * part + jj;
-  }
-  if (t >= ntiles) return;
-  const int4 d = tdesc[t < n0 ? lo0 + t : lo1 + (t - n0)];
+  auto tile_of = [&](int j, int& t) -> bool {
+    if (!unit) {
+      const int chunk = (ntiles + 7) >> 3;
+      if (j >= chunk) return false;
+      t = xcd * chunk + j;
+    } else if (j < full) {
+      t = ((j / unit) * 8 + xcd) * unit + j % unit;
+    } else {
+      const int rest = ntiles - 8 * full, part = (rest + 7) >> 3, jj = j - full;
+      if (jj >= part) return false;
+      t = 8 * full + xcd * part + jj;
+    }
+    return t < ntiles;
+  };
+  // The counter is an atomic in the XCD's L2 (its workgroups are the ones
+  // that use it), on a cache line of its own.  Every lane issues the claim;
+  // only thread 0's offset lies inside the 4-byte resource, so the count
+  // rises by one per tile and no branch holds the result (a divergent one
+  // made the compiler wait for the atomic at once).
+  __shared__ int s_claim;
+  const rsrc_t claim_rs = make_rsrc(w.claims + 32 * (8 * (GATE_UP ? 0 : 1) + xcd), 4u);
+  const int claim_off = threadIdx.x == 0 ? 0 : 4;
+  auto claim = [&]() { return __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, claim_rs, claim_off, 0, 0); };
+  int next_claim = 0;   // thread 0: the claim requested during the current tile
+
+  auto body = [&](const int t) {
+  // (PERSIST runs without a window or slot map.)
+  const int4 d = PERSIST ? tdesc[t] : tdesc[t < n0 ? lo0 + t : lo1 + (t - n0)];
   const int g = uni(d.x), seg0 = uni(d.y), nrows = uni(d.z);
   const int m0 = uni(d.w & 0xFFFF) * BM, nt = uni(d.w >> 16);
   const bool shared = g == E;
   // Weight block of the group: its expert index, or its cache slot.
-  const int gw = (slot_map && !shared) ? uni(slot_map[g]) : g;
+  const int gw = (!PERSIST && slot_map && !shared) ? uni(slot_map[g]) : g;
   const int kdim = GATE_UP ? H : (shared ? L.Is : L.I);
   const int inner_n = shared ? L.Is : L.I;           // gate_up: inner rows of the group
   const int nreal = kdim / BK;                       // real k-steps
@@ -305,6 +327,10 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
   issue(wb[0], 0, 0);
   issue(wb[1], 1, 1);
   issue(wb[2], 2, 2);
+  // The next claim, behind the first three steps' loads: a wait for the token
+  // indices above would otherwise wait for the atomic too (the counter
+  // retires loads in order); by step 2 it has returned.
+  if constexpr (PERSIST) next_claim = claim();
   // One k-step.  YOUNGER: loads of later steps already issued when this one
   // starts (two, except in the last two steps), kVmPerStep per step and wave;
   // ISSUE: whether this step requests step ks + 3.  Both are compile-time
@@ -418,6 +444,31 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
     const u32x4 v = *reinterpret_cast<const u32x4*>(ep + row * kCols + 8 * cc);
     __builtin_amdgcn_raw_buffer_store_b128(v, ors, (uint32_t)row * ostride + 2u * ocol + 16u * cc, 0, 0);
   }
+  };
+
+  if constexpr (!PERSIST) {
+    int t;
+    if (!tile_of(j8, t)) return;
+    body(t);
+  } else {
+    // Every wave has read s_claim before it passes the first barrier of the
+    // tile, and thread 0 rewrites it only after the tile's last one.  The
+    // barrier after the rewrite also keeps the next tile's loads into the
+    // ring off the epilogue tiles until every wave has stored its part.
+    // (lgkmcnt(0): thread 0's LDS write has completed before the barrier.)
+    const int first = claim();
+    if (threadIdx.x == 0) s_claim = first;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier();
+    int t;
+    for (int j = uni(s_claim); tile_of(j, t);) {
+      body(t);
+      if (threadIdx.x == 0) s_claim = next_claim;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      barrier();
+      j = uni(s_claim);
+    }
+  }
 }
 
 // out[t] = bf16( sum_k w[t, k] y[slot_of(t, k)] + gate[t] y[T*K + t] ), k in
@@ -507,9 +558,12 @@ static bool stream_weights(const LayerArgs& L, int T) { return (int64_t)T * L.K 
 // smallest batches, 192 x 256 with eight waves for the largest, else
 // 160 x 128), weight cache policy by stream_weights.
 template <bool GATE_UP>
-static auto gemm_kernel_for(const LayerArgs& L, int T) {
+static auto gemm_kernel_for(const LayerArgs& L, int T, bool persist) {
   if (gemm_small_rows(T, L.K, L.E)) return grouped_gemm_kernel<GATE_UP, kNonTemporal, kGemmBMSmall, 4>;
-  if (GATE_UP && gemm_wide(T, L.K, L.E)) return grouped_gemm_kernel<GATE_UP, 0, kGemmBMWide, 8>;
+  if constexpr (GATE_UP) {
+    if (gemm_wide(T, L.K, L.E))
+      return persist ? grouped_gemm_kernel<true, 0, kGemmBMWide, 8, true> : grouped_gemm_kernel<true, 0, kGemmBMWide, 8>;
+  }
   return stream_weights(L, T) ? grouped_gemm_kernel<GATE_UP, kNonTemporal, kGemmBM, 4>
                               : grouped_gemm_kernel<GATE_UP, 0, kGemmBM, 4>;
 }
@@ -529,8 +583,13 @@ hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work
   // them then compile to scalar loads.
   const int64_t bound = gemm_tile_bound(T, L.K, L.E, 2 * L.I, 2 * L.Is);
   const int unit = gemm_units(L, T) ? gemm_unit(gemm_per_cu(L, T, true), num_cus) : 0;
-  auto k = gemm_kernel_for<true>(L, T);
-  hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(gemm_threads(L, T, true)), 0, s, L, x, T, w, (const int*)w.tiles_gu,
+  // The large-batch tiles run persistent (one workgroup per CU claiming its
+  // XCD's tiles), except over a window of the streamed path, whose rounds
+  // would need their own counters.
+  const bool persist = !window && !slot_map && gemm_wide(T, L.K, L.E);
+  auto k = gemm_kernel_for<true>(L, T, persist);
+  const unsigned grid = persist ? (unsigned)(8 * ((std::max(num_cus, 8) + 7) / 8)) : gemm_grid(bound, unit);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(gemm_threads(L, T, true)), 0, s, L, x, T, w, (const int*)w.tiles_gu,
                      (const int4*)w.tdesc_gu, (const int*)w.slot_tok, window, slot_map, unit);
   return hipGetLastError();
 }
@@ -549,7 +608,7 @@ hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hi
     const int64_t ug = gemm_unit(gemm_per_cu(L, T, true), num_cus);
     unit = (int)std::max<int64_t>(1, ug * ndn * bmg / (ngu * bmd));
   }
-  auto k = gemm_kernel_for<false>(L, T);
+  auto k = gemm_kernel_for<false>(L, T, false);
   hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(gemm_threads(L, T, false)), 0, s, L, (const bf16_t*)nullptr, T, w,
                      (const int*)w.tiles_dn, (const int4*)w.tdesc_dn, (const int*)w.slot_tok, window, slot_map, unit);
   return hipGetLastError();

@@ -93,6 +93,7 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   c.w.offsets = (int32_t*)take((E + 1) * 4);
   c.w.tiles_gu = (int32_t*)take((E + 2) * 4);
   c.w.tiles_dn = (int32_t*)take((E + 2) * 4);
+  c.w.claims = (int32_t*)take(2 * 8 * 128);
   c.w.tdesc_gu = (int4*)take((size_t)moe::gemm_tile_bound(T, (int)K, (int)E, 2 * (int)I, 2 * (int)Is) * 16);
   c.w.tdesc_dn = (int4*)take((size_t)moe::gemm_tile_bound(T, (int)K, (int)E, (int)H, (int)H) * 16);
   c.w.perm = (int32_t*)take(tk * 4);
