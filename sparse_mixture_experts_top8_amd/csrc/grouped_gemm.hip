@@ -238,7 +238,12 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
   const int nsteps = ((nreal + NS - 1) / NS) * NS;   // padded to the ring depth (padding: zero weights)
   const int rows_here = min(BM, nrows - m0);         // rows of this tile inside the group (>= 1)
 
-  const int tid = threadIdx.x;
+  // The thread index is made opaque once per tile so that the persistent
+  // loop recomputes the lane-dependent offsets below instead of holding them
+  // across tiles (where they were spilled).
+  int tid_ = (int)threadIdx.x;
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid_));
+  const int tid = tid_;
   const int wave = tid >> 6, lane = tid & 63;
   const int wv = uni(wave);
   const int l16 = lane & 15, q = lane >> 4;
