@@ -31,6 +31,7 @@
 // everything else uses router_select_tok_kernel (one wave per token; block
 // histograms by integer atomics where the dispatch needs them).
 #include "kernels.hpp"
+#include "lds_pipe.hpp"
 
 namespace moe {
 
@@ -138,6 +139,141 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + 16 * i + 4 * (lane >> 4) + r;
+          if (t < T) out[(size_t)t * Ep + e] = acc[i][jj][r];
+        }
+    }
+  }
+}
+
+// The same logits for tiles of 32, 64 or 128 tokens, with the tile's x rows
+// staged in LDS: each 64-wide k-step of them goes to LDS once by direct-to-LDS
+// loads (a four-stage ring, three steps in flight, the row swizzle of the
+// grouped GEMMs) and every wave reads its MFMA operands from there, while its
+// router rows stream through registers.  Where each wave loaded the x rows
+// itself, the four waves' copies met only in the 32 KB L1 (a deeper register
+// ring was slower: zipf16384 router 78 -> 87 us).  Per accumulator the MFMAs
+// run in the same k order, so the sums are the same.
+template <int kTB>
+__global__ __launch_bounds__(256, 1) void router_logits_lds_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
+                                                                  int ksplit, float* __restrict__ part,
+                                                                  int* __restrict__ hist_zero, int hist_n,
+                                                                  uint32_t* __restrict__ ctl, uint32_t tag) {
+  using namespace pipe;
+  constexpr int NS = 4;
+  constexpr int kRows = 16 * kTB, kStage = kRows * 128;
+  constexpr int kDma = kRows * 8 / 256;              // direct-to-LDS instructions per wave per step
+  constexpr int kVm = kDma + 2 * kColBlocks;         // loads per wave per step
+  static_assert(kDma >= 1 && 3 * kVm <= 63, "x rows and router rows per step");
+  __shared__ __attribute__((aligned(1024))) char lds[NS * kStage];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (ctl && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) ctl[kCtlLast] = tag;
+  if (hist_zero) {
+    const int nwg = gridDim.x * gridDim.y, wg = blockIdx.y * gridDim.x + blockIdx.x;
+    for (int i = wg * 256 + tid; i < hist_n; i += nwg * 256) hist_zero[i] = 0;
+  }
+  const int t0 = blockIdx.x * kRows, s = blockIdx.y;
+  const int H = L.H, E = L.E, Ep = router_cols(E);
+  const int nsub = (E + 1 + 15) >> 4;
+  const int wv = uni(wave);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int klen = H / ksplit, kbeg = s * klen, nk = klen / 64;
+  const int nsteps = ((nk + NS - 1) / NS) * NS;     // padded to the ring; padding steps add nothing
+  const uint32_t lds_base = (uint32_t)(size_t)(lds_ptr_t)lds;
+
+  // x rows: instruction j of wave w writes row 8 (4 j + w) + lane / 8 of a
+  // stage, stored chunk lane % 8 holding chunk (lane % 8) ^ swz(row); rows
+  // past T repeat row T - 1 (their outputs are dropped).
+  const bf16_t* a_src[kDma];
+#pragma unroll
+  for (int j = 0; j < kDma; ++j) {
+    const int r = 8 * (4 * j + wv) + (lane >> 3);
+    a_src[j] = x + (size_t)min(t0 + r, T - 1) * H + kbeg + ((lane & 7) ^ lds_swizzle(r)) * 8;
+  }
+  // Router rows of the wave's column blocks wave + 4 jj (rows past E + 1
+  // repeat row E; blocks past the last are loaded, not used, so every wave
+  // issues the same loads); lane quarter q reads elements 16 q .. 16 q + 15.
+  const bf16_t* brow[kColBlocks];
+#pragma unroll
+  for (int jj = 0; jj < kColBlocks; ++jj) {
+    const int e = min(16 * (wv + 4 * jj) + r16, E);
+    brow[jj] = (e < E ? L.router_w + (size_t)e * H : L.sh_expert_gate) + kbeg + 16 * q;
+  }
+  u32x4 wb[NS][kColBlocks][2];
+  auto issue = [&](u32x4 (&wbs)[kColBlocks][2], int st, int ks) {
+    const int kv = min(ks, nk - 1);
+#pragma unroll
+    for (int j = 0; j < kDma; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + 64 * kv), (lds_ptr_t)(lds + st * kStage + 1024 * (4 * j + wv)),
+                                       16, 0, 0);
+#pragma unroll
+    for (int jj = 0; jj < kColBlocks; ++jj)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) wbs[jj][h] = ld16(brow[jj] + 64 * kv + 8 * h);
+  };
+  f32x4 acc[kTB][kColBlocks];
+#pragma unroll
+  for (int i = 0; i < kTB; ++i)
+#pragma unroll
+    for (int jj = 0; jj < kColBlocks; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(wb[0], 0, 0);
+  issue(wb[1], 1, 1);
+  issue(wb[2], 2, 2);
+  // One k-step (YOUNGER: steps already requested after this one; ISSUE:
+  // whether it requests step ks + 3), as in grouped_gemm_kernel.
+  auto step = [&](auto younger_c, auto issue_c, u32x4 (&wcur)[kColBlocks][2], u32x4 (&wnext)[kColBlocks][2], int st,
+                  int ks) {
+    wait_vm<decltype(younger_c)::value * kVm>();
+    barrier();
+    if constexpr (decltype(issue_c)::value) issue(wnext, (st + 3) % NS, ks + 3);
+    if (ks < nk) {
+      const uint32_t sa0 = lds_base + st * kStage + r16 * 128 + (((2 * q) ^ lds_swizzle(r16)) << 4);
+      const uint32_t sa1 = lds_base + st * kStage + r16 * 128 + (((2 * q + 1) ^ lds_swizzle(r16)) << 4);
+      u32x4 X[kTB], Y[kTB];
+      lds_read_group<0>(X, sa0, std::make_integer_sequence<int, kTB>{});
+      lds_read_group<0>(Y, sa1, std::make_integer_sequence<int, kTB>{});
+      wait_lds_keep<kTB>(X);
+#pragma unroll
+      for (int jj = 0; jj < kColBlocks; ++jj)
+        if (wv + 4 * jj < nsub)
+#pragma unroll
+          for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(X[i], wcur[jj][0], acc[i][jj]);
+      wait_lds_keep<0>(Y);
+#pragma unroll
+      for (int jj = 0; jj < kColBlocks; ++jj)
+        if (wv + 4 * jj < nsub)
+#pragma unroll
+          for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(Y[i], wcur[jj][1], acc[i][jj]);
+    }
+  };
+  using c0 = std::integral_constant<int, 0>;
+  using c1 = std::integral_constant<int, 1>;
+  using c2 = std::integral_constant<int, 2>;
+  using yes = std::true_type;
+  using no = std::false_type;
+  int k4 = 0;
+  for (; k4 + NS < nsteps; k4 += NS) {
+    step(c2{}, yes{}, wb[0], wb[3], 0, k4);
+    step(c2{}, yes{}, wb[1], wb[0], 1, k4 + 1);
+    step(c2{}, yes{}, wb[2], wb[1], 2, k4 + 2);
+    step(c2{}, yes{}, wb[3], wb[2], 3, k4 + 3);
+  }
+  step(c2{}, yes{}, wb[0], wb[3], 0, k4);
+  step(c2{}, no{}, wb[1], wb[0], 1, k4 + 1);
+  step(c1{}, no{}, wb[2], wb[1], 2, k4 + 2);
+  step(c0{}, no{}, wb[3], wb[2], 3, k4 + 3);
+
+  // D[4 (lane / 16) + r][lane % 16] of each 16 x 16 block.
+  float* out = part + (size_t)s * T * Ep;
+#pragma unroll
+  for (int jj = 0; jj < kColBlocks; ++jj) {
+    const int e = 16 * (wv + 4 * jj) + r16;
+    if (wv + 4 * jj < nsub && e <= E) {
+#pragma unroll
+      for (int i = 0; i < kTB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 16 * i + 4 * q + r;
           if (t < T) out[(size_t)t * Ep + e] = acc[i][jj][r];
         }
     }
@@ -426,13 +562,13 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
     hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
                        w.call_tag);
   else if (tile == 32)
-    hipLaunchKernelGGL(router_logits_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+    hipLaunchKernelGGL(router_logits_lds_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
                        w.call_tag);
   else if (tile == 64)
-    hipLaunchKernelGGL(router_logits_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+    hipLaunchKernelGGL(router_logits_lds_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
                        w.call_tag);
   else
-    hipLaunchKernelGGL(router_logits_kernel<8>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+    hipLaunchKernelGGL(router_logits_lds_kernel<8>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
                        w.call_tag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
