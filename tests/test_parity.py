@@ -244,6 +244,33 @@ def test_toy_empty_and_determinism(toy):
     assert torch.equal(outp.view(torch.int16).cpu(), a.view(torch.int16).cpu()[p])
 
 
+def test_toy_wide_workspace_reuse(toy):
+    """Large batches (T K >= 2 E 160) run gate_up persistent, each workgroup
+    claiming tiles from a per-XCD counter in the workspace that the dispatch
+    zeroes on every call.  One workspace, filled with 0xA5 bytes first, serves
+    large batches of different sizes in turn (single- and multi-launch
+    dispatch) with a smaller batch between them; every call is bit-identical
+    to the same call on a fresh workspace, and one is checked against the
+    oracle."""
+    moe = _moe()
+    d, bits, layer = toy
+    Ts = [6000, 1300, 2048, 200, 6000, 2049]
+    need = max(layer.workspace_bytes(T) for T in Ts)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    for i, T in enumerate(Ts):
+        _say(f"case toy workspace reuse call {i} T={T}")
+        xb = mi.make_x(d, T, 5100 + T)
+        x = moe.bits_to_device(xb, "cuda")
+        a = moe.forward(x, layer, ws=ws)
+        b = moe.forward(x, layer)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"T={T} (call {i}) differs from a fresh workspace"
+        if i == 1:
+            r, out = run_layer(layer, xb)
+            gi = check_routing(xb, bits, d, r, f"toy reuse T={T}")
+            check_output(xb, bits, d, gi, _np(a.float()), np.arange(T), f"toy reuse T={T}")
+
+
 # ---------------------------------------------------------------------------
 # Full shape (H=2048, E=256, K=8, I=Is=512).
 # ---------------------------------------------------------------------------
