@@ -18,7 +18,8 @@
 // overlaps the other's streaming.  Batches of a few rows per expert use
 // 32-row tiles, four workgroups per CU; batches of many (two 160-row tiles
 // per expert on average) run gate_up in 192 x 256 tiles of eight waves, one
-// workgroup per CU (the down projection keeps 160 x 128).  Wave w owns weight
+// persistent workgroup per CU that claims its XCD's tiles in turn (the down
+// projection keeps 160 x 128, one workgroup per tile).  Wave w owns weight
 // rows 32w .. 32w + 31 of the tile as two 16-column MFMA blocks: for gate_up
 // the gate rows and the up rows of the same 16 inner rows (SiLU(g) * u is
 // formed in registers, both blocks having the same layout), for down 32 output
@@ -31,7 +32,9 @@
 // loads (global_load_lds_dwordx4).  Within a k-step, lane quarter q (lane / 16)
 // covers k 16q .. 16q + 15, eight per MFMA k-step; activations and weights
 // use the same order, so the products are unchanged and each lane reads 32
-// contiguous bytes of a weight row per step.
+// contiguous bytes of a weight row per step.  The LDS operands of a step are
+// read in groups, each group's reads issued before the MFMAs of the group
+// ahead of it.
 //
 // LDS rows of the activation tile are 128 bytes; the 16-byte chunk c of row r
 // is stored at chunk c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  A
@@ -136,8 +139,8 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
   //
   // PERSIST: one workgroup per CU instead, each taking the tiles its XCD would
   // have run, in the same order, through a per-XCD counter (j = the number of
-  // tiles that XCD's workgroups took before); the next claim is requested at
-  // the start of each tile.  With one eight-wave workgroup per CU a new
+  // tiles that XCD's workgroups took before); the next claim is requested
+  // during each tile.  With one eight-wave workgroup per CU a new
   // workgroup started ~2.2 us after the last one ended, plus ~0.8 us for the
   // tile count and descriptor (MI355X, Zipf(1.1) over 16384 tokens, ~14 tiles
   // per CU).
@@ -157,9 +160,11 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
     }
     return t < ntiles;
   };
-  // The counter is an atomic in the XCD's L2 (its workgroups are the ones
-  // that use it), on a cache line of its own.  Every lane issues the claim;
-  // only thread 0's offset lies inside the 4-byte resource, so the count
+  // Each counter sits on a 128-byte line of its own and is used by one XCD's
+  // workgroups.  The claim is an atomic add with return of device scope (no
+  // sc1 bit, as the compiler emits its own agent-scope atomics on gfx950), so
+  // a count is right whichever XCD a workgroup runs on.  Every lane issues
+  // it; only thread 0's offset lies inside the 4-byte resource, so the count
   // rises by one per tile and no branch holds the result (a divergent one
   // made the compiler wait for the atomic at once).
   __shared__ int s_claim;

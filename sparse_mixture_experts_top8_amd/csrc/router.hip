@@ -13,17 +13,19 @@
 // the same quantity as a softmax over the K selected logits alone (the full
 // denominator cancels); the kernel computes the latter.
 //
-// Two kernels.  router_logits_kernel: one workgroup per (64-token tile, or
-// 32-token tile for small batches and 128-token tile for large ones, slice of
-// H); the shared gate row rides
-// along as column E, so the E + 1 columns are 17 MFMA column blocks of 16.
-// Each wave streams its column blocks' rows and the tile's x rows through a
-// two-step register pipeline of 64-wide k-steps (each row's whole 128-byte
-// line per step) and writes fp32 partial sums (one fp32 accumulator chain of
-// at most H / 32 MFMAs per slice).  For large batches the router is read
-// once per 64 tokens: its re-reads through L2, not the arithmetic, set the
-// kernel's pace.  Small batches split H into up to H/64 slices so that the
-// launch still spans the chip.
+// Logits: one workgroup per (64-token tile, or 16- or 32-token tile for small
+// batches and 128-token tile for large ones, slice of H); the shared gate row
+// rides along as column E, so the E + 1 columns are 17 MFMA column blocks of
+// 16.  Each wave owns column blocks w, w + 4, ... and streams their router rows
+// through registers in 64-wide k-steps (each row's whole 128-byte line per
+// step), writing fp32 partial sums (one fp32 accumulator chain of at most
+// H / 32 MFMAs per slice).  The tile's x rows go to LDS once per k-step and
+// every wave reads them there (router_logits_lds_kernel, tiles of 32 tokens
+// and more); 16-token tiles load them per wave (router_logits_kernel).  For
+// large batches the router is read once per 64 or 128 tokens through L2.
+// Small batches split H into up to H/64 slices so that the launch still spans
+// the chip.
+// Selection, two kernels.
 // router_select_kernel (for the load-balance statistic, which needs its
 // per-block probability sums): one workgroup of 16 waves per 32 tokens sums
 // the slices in a fixed order and selects, two tokens per wave, and writes
@@ -45,7 +47,7 @@ constexpr int kLargeT = 8192;            // from this many tokens: 128-token log
                                          // read half as often; zipf16384 router 90 -> 80 us, while at
                                          // 4096 tokens the extra H slices cost more than that saves)
 constexpr int kColBlocks = 5;            // column blocks per wave (17 for E = 256, plus the gate column)
-constexpr int kDepth = 2;                // 64-wide k-steps in flight per wave
+constexpr int kDepth = 2;                // 64-wide k-steps in flight per wave (router_logits_kernel)
 constexpr int kMaxRouterCols = 260;      // router_cols(256)
 
 // kTB 16-token blocks per workgroup.
