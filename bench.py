@@ -411,13 +411,10 @@ def measure(moe, mi, name, steps, warmup, nlayers, base_bits, args, headline=Fal
         torch.cuda.synchronize()
         return round(start.elapsed_time(end) / n * 1e3, 2)
 
-    others = {}
-    if not args.layer_only:
-        others = other_entry_points(moe, mi, d, wl, T, steps, warmup, nlayers, layers, xs, outs, ws, time_calls)
-
-    # Kernel attribution: the same steps again, each recording six events at
-    # its phase boundaries on the same stream (the fused decode path records
-    # its single kernel between events 0 and 1).
+    # Kernel attribution: the same steps again, right after the timed region
+    # (the GPU at the same clock), each recording six events at its phase
+    # boundaries on the same stream (the fused decode path records its single
+    # kernel between events 0 and 1).
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     for e6 in ev:
         for e in e6:
@@ -437,6 +434,12 @@ def measure(moe, mi, name, steps, warmup, nlayers, base_bits, args, headline=Fal
         phase_ms = {"decode_fused": ms_per_step}
     log("  phase us: " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in phase_ms.items())
         + f"; step {ms_per_step * 1e3:.1f} us (repeats " + ", ".join(f"{r * 1e3:.1f}" for r in reps) + ")")
+
+    # The other entry points after the attribution: the streamed one leaves
+    # the GPU idle behind host copies for tens of milliseconds per call.
+    others = {}
+    if not args.layer_only:
+        others = other_entry_points(moe, mi, d, wl, T, steps, warmup, nlayers, layers, xs, outs, ws, time_calls)
 
     step_bytes, step_flops = step_work(d, T, U_mean)
     dom = max(phase_ms, key=phase_ms.get)

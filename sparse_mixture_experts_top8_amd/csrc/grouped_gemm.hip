@@ -295,8 +295,8 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
     constexpr int YOUNGER = decltype(younger_c)::value;
     wait_vm<YOUNGER * kVmPerStep>();   // this step's loads have landed
     barrier();   // every wave's part of the stage is in LDS; the stage read last step is free
-    // Step ks + 3 is requested here, or for eight-wave tiles after the first
-    // group's MFMAs (see below).
+    // Step ks + 3 is requested here, or for eight-wave tiles ahead of the
+    // last group's MFMAs (see below).
     constexpr bool kLateIssue = NW == 8;
     if constexpr (decltype(issue_c)::value && !kLateIssue) issue(wnext, (st + 3) % NS, ks + 3);
     const uint32_t sa0 = lds_base + st * kATile + l16 * 128 + (((2 * q) ^ lds_swizzle(l16)) << 4);
@@ -315,23 +315,26 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
     // leave the barrier together, do not wait for LDS at the same time.  The
     // second group's MFMAs are skipped when the tile's rows end before it
     // (uniform branch); its reads are not.  Eight-wave tiles request step
-    // ks + 3 after the first group's MFMAs, not ahead of them: a wave whose
-    // load stalls on a full address queue then has MFMAs in flight (MI355X,
-    // Zipf(1.1) over 16384 tokens: gate_up 651 -> 630 us over three repeats).
-    // The four-wave tiles measured 1-4 us slower that way.
+    // ks + 3 ahead of the last group's MFMAs, not ahead of the first: a wave
+    // whose load stalls on a full address queue then has MFMAs in flight, and
+    // the loads still have two steps to land (MI355X, Zipf(1.1) over 16384
+    // tokens, gate_up averaged over three repeats on one box: 622 us after
+    // the first group, 614 after the second, 608 after the third, 630 at the
+    // end of the step; ahead of the first group was 21 us slower than after
+    // it).  The four-wave tiles measured 1-4 us slower with any late request.
     u32x4 X[kGroup], Y[kGroup];
     if constexpr (kMBlocks > kGroup) {
       lds_read_group<0>(X, sa0, seq{});
       lds_read_group<kGroup>(Y, sa0, seq{});
       wait_lds_keep<kGroup>(X);
       mma(0, 0, X);
-      if constexpr (decltype(issue_c)::value && kLateIssue) issue(wnext, (st + 3) % NS, ks + 3);
       lds_read_group<0>(X, sa1, seq{});
       wait_lds_keep<kGroup>(Y);
       if (mblocks > kGroup) mma(kGroup, 0, Y);
       lds_read_group<kGroup>(Y, sa1, seq{});
       wait_lds_keep<kGroup>(X);
       mma(0, 1, X);
+      if constexpr (decltype(issue_c)::value && kLateIssue) issue(wnext, (st + 3) % NS, ks + 3);
       wait_lds_keep<0>(Y);
       if (mblocks > kGroup) mma(kGroup, 1, Y);
     } else {
