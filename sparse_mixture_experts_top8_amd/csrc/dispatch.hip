@@ -99,14 +99,15 @@ __device__ void dispatch_tiles(LayerArgs L, int T, const Work& w, int g) {
   const int mtg = (nrows + bmg - 1) / bmg, mtd = (nrows + bmd - 1) / bmd;
   const int ngu = (2 * (shared ? L.Is : L.I) + bng - 1) / bng, ndn = L.H / bnd;
   const int bgu = w.tiles_gu[g], bdn = w.tiles_dn[g];
+  const int rbg = gemm_row_block(T, L.K, E, true), rbd = gemm_row_block(T, L.K, E, false);
   for (int i = threadIdx.x; i < mtg * ngu; i += 256) {
     int mi, nt;
-    gemm_tile_order(i, mtg, ngu, mi, nt);
+    gemm_tile_order(i, mtg, ngu, rbg, mi, nt);
     w.tdesc_gu[bgu + i] = make_int4(g, seg0, nrows, mi | (nt << 16));
   }
   for (int i = threadIdx.x; i < mtd * ndn; i += 256) {
     int mi, nt;
-    gemm_tile_order(i, mtd, ndn, mi, nt);
+    gemm_tile_order(i, mtd, ndn, rbd, mi, nt);
     w.tdesc_dn[bdn + i] = make_int4(g, seg0, nrows, mi | (nt << 16));
   }
 }
@@ -225,6 +226,7 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
   {
     const int ngu_r = (2 * L.I + bng - 1) / bng, ngu_s = (2 * L.Is + bng - 1) / bng;
     const int ndn = L.H / bnd, gumax = max(ngu_r, ngu_s), ncols = gumax + ndn;
+    const int rbg = gemm_row_block(T, L.K, E, true), rbd = gemm_row_block(T, L.K, E, false);
     for (int c = wave; c < ncols; c += kSmallThreads / 64) {
       for (int g = lane; g <= E; g += 64) {
         const bool shared = g == E, gu = c < gumax;
@@ -232,10 +234,10 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(LayerArgs
         if (nt >= ncol) continue;
         const int seg0 = shared ? 0 : s_off[g];
         const int nrows = shared ? T : s_cnt[g];
-        const int bm = gu ? bmg : bmd, mt = (nrows + bm - 1) / bm;
+        const int bm = gu ? bmg : bmd, mt = (nrows + bm - 1) / bm, rb = gu ? rbg : rbd;
         int4* base = gu ? w.tdesc_gu + s_tgu[g] : w.tdesc_dn + s_tdn[g];
-        for (int b0 = 0; b0 < mt; b0 += kGemmRowBlock) {
-          const int rows = min(kGemmRowBlock, mt - b0);
+        for (int b0 = 0; b0 < mt; b0 += rb) {
+          const int rows = min(rb, mt - b0);
           int4* d = base + b0 * ncol + nt * rows;
           for (int r = 0; r < rows; ++r) d[r] = make_int4(g, seg0, nrows, (b0 + r) | (nt << 16));
         }

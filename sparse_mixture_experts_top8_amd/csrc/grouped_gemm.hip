@@ -52,10 +52,11 @@
 // Scheduling: workgroups are handed to the eight XCDs round-robin (workgroup i
 // on XCD i % 8); the tile list is cut into eight contiguous ranges and XCD x
 // takes range x in order, or for large batches dealt to the XCDs in units
-// (see the kernel).  Within a group, tiles come in blocks of eight row
-// tiles, column tile major inside a block (gemm_tile_order): a block's row
-// tiles of one weight slab, and its column tiles of one activation block, run
-// side by side in one XCD and share them through its L2.
+// (see the kernel).  Within a group, tiles come in blocks of row tiles,
+// column tile major inside a block (gemm_tile_order; eight row tiles per
+// block, one for the 160- and 32-row gate_up tiles): a block's row tiles of
+// one weight slab, and its column tiles of one activation block, run side by
+// side in one XCD and share them through its L2.
 #include "kernels.hpp"
 #include "lds_pipe.hpp"
 

@@ -49,27 +49,37 @@ __host__ __device__ inline int64_t gemm_tile_bound(int64_t T, int K, int E, int 
   return a > b ? a : b;
 }
 
-// Order of a group's mt x nct tiles in the dispatch list: blocks of
-// kGemmRowBlock row tiles, within a block column tile major and row tile
-// minor.  Consecutive tiles run side by side on one XCD, so a block's
+// Order of a group's mt x nct tiles in the dispatch list: blocks of rb row
+// tiles, within a block column tile major and row tile minor (rb = 1: row
+// tile major).  Consecutive tiles run side by side on one XCD, so a block's
 // activation rows are fetched once for all its column tiles and its weight
 // columns once for all its row tiles (through that XCD's L2); a group of at
-// most kGemmRowBlock row tiles is simply column tile major.
+// most rb row tiles is simply column tile major.  The down projection and the
+// large-batch gate_up take blocks of eight row tiles.  The other gate_up
+// tiles go row tile major: the shared expert's gate/up weights (2 MB) stay
+// in L2 across all its row tiles anyway, and its x rows are then shared by
+// consecutive tiles (MI355X, 4096 tokens, gate_up over three alternating
+// repeats: 240-244 -> 234-240 us).  Row tile major measured slower for the
+// down projection (Zipf(1.1) over 16384 tokens: 410-414 -> 429-430 us) and
+// for the large-batch gate_up (617-620 -> 624-630 us).
 constexpr int kGemmRowBlock = 8;
-__host__ __device__ inline void gemm_tile_order(int i, int mt, int nct, int& mi, int& nt) {
-  const int full = (mt / kGemmRowBlock) * kGemmRowBlock * nct;   // tiles of the full row blocks
+__host__ __device__ inline int gemm_row_block(int64_t T, int K, int E, bool gate_up) {
+  return gate_up && !gemm_wide(T, K, E) ? 1 : kGemmRowBlock;
+}
+__host__ __device__ inline void gemm_tile_order(int i, int mt, int nct, int rb, int& mi, int& nt) {
+  const int full = (mt / rb) * rb * nct;   // tiles of the full row blocks
   int b, rows, j;
   if (i < full) {
-    b = i / (kGemmRowBlock * nct);
-    rows = kGemmRowBlock;
-    j = i - b * kGemmRowBlock * nct;
+    b = i / (rb * nct);
+    rows = rb;
+    j = i - b * rb * nct;
   } else {
-    b = mt / kGemmRowBlock;
-    rows = mt - b * kGemmRowBlock;
+    b = mt / rb;
+    rows = mt - b * rb;
     j = i - full;
   }
   nt = j / rows;
-  mi = b * kGemmRowBlock + (j - nt * rows);
+  mi = b * rb + (j - nt * rows);
 }
 
 __host__ __device__ inline int router_blocks(int64_t T) { return (int)((T + kRouterTokens - 1) / kRouterTokens); }
