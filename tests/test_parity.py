@@ -935,6 +935,8 @@ def test_full_gemm_tile_regimes(full):
     # Both sides of each switch of the grouped GEMMs at full shape: 32-row
     # tiles up to 8 slots per expert on average (256 tokens), 160-row tiles
     # with streamed weight loads up to 16 (512 tokens), then plain loads.
+    # 256 tokens (2048 pairs) is also the last batch dispatched by one
+    # workgroup per group, 257 the first by a single workgroup.
     # Every row against the oracle, and the tiled expert layout bitwise equal
     # to the row-major one.
     moe = _moe()
