@@ -196,7 +196,7 @@ struct Work {
   int32_t* perm;       // [T*K]
   int32_t* slot_tok;   // [T*K]  token of each slot (perm / K)
   int32_t* slot_of;    // [T*K]
-  bf16_t* h;           // [T*K, I]
+  bf16_t* h;           // [T*K, I]  (its first E words hold the pairs per expert during the multi-launch dispatch)
   bf16_t* h_sh;        // [T, Is]
   bf16_t* y;           // [T*K + T, H]  weighted expert outputs, routed slots then shared rows
   float* psum;         // [nblk * E]  per router block: sum over its tokens of each expert's softmax probability
