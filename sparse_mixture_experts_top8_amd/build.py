@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["router.hip", "dispatch.hip", "grouped_gemm.hip", "decode.hip", "norm.hip", "stream.hip", "pack.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "route.hip", "dispatch.hip", "grouped_gemm.hip", "decode.hip", "norm.hip", "stream.hip", "pack.hip", "moe_api.cpp"]
 
 # Packed fp32 instructions are switched off: hipcc would otherwise form
 # v_pk_* fp32 ops from plain float code.

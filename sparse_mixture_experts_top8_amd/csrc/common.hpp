@@ -206,6 +206,7 @@ struct Work {
   int32_t* st_win_dn;  // [E][4]   the same for the down projection
   bf16_t* xn;          // [T, H]  RMSNorm of the sub-block input (block form)
   uint32_t* ctl;       // control block at the start of the workspace (kCtlLast is written)
+  uint64_t* lt;        // tagged exchange region after it (fused small-batch route: logits, selections)
   uint32_t call_tag;   // this call's tag
 };
 

@@ -103,7 +103,8 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
                                                              const int4* __restrict__ tdesc,
                                                              const int* __restrict__ slot_tok,
                                                              const int* __restrict__ window,
-                                                             const int* __restrict__ slot_map, int unit) {
+                                                             const int* __restrict__ slot_map, int unit,
+                                                             int tile_bound) {
   using S = TileShape<BM, NW>;
   constexpr int kATile = S::kATile, kMBlocks = S::kMBlocks, kGroup = S::kGroup, kADma = S::kADma;
   constexpr int kVmPerStep = S::kVmPerStep, BN = S::kBN;
@@ -121,7 +122,12 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
     lo1 = uni(window[2]);
     ntiles = n0 + uni(window[3]);
   } else {
-    ntiles = uni(prefix[E + 1]);
+    // Clamped to the tile bound, as every table field below is clamped to
+    // its range: when a fused route's bounded wait gives up (the call then
+    // reports MOE_ERR_TIMEOUT), its workgroups may have written tables from
+    // different views of the selections; results are wrong, but no access
+    // leaves its array.  With consistent tables the clamps change nothing.
+    ntiles = min(max(uni(prefix[E + 1]), 0), tile_bound);   // tile_bound: gemm_tile_bound of this GEMM
     n0 = ntiles;
   }
   // unit == 0: XCD x takes the x-th contiguous eighth of the tile list, in
@@ -177,9 +183,13 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
   auto body = [&](const int t) {
   // (PERSIST runs without a window or slot map.)
   const int4 d = PERSIST ? tdesc[t] : tdesc[t < n0 ? lo0 + t : lo1 + (t - n0)];
-  const int g = uni(d.x), seg0 = uni(d.y), nrows = uni(d.z);
-  const int m0 = uni(d.w & 0xFFFF) * BM, nt = uni(d.w >> 16);
+  const int g = min(max(uni(d.x), 0), E);
   const bool shared = g == E;
+  const int nrows = min(max(uni(d.z), 1), shared ? T : T * K);
+  const int seg0 = shared ? 0 : min(max(uni(d.y), 0), T * K - nrows);
+  const int m0 = min(uni(d.w & 0xFFFF), (nrows - 1) / BM) * BM;
+  const int nt = min(max(uni(d.w >> 16), 0),
+                     (GATE_UP ? (2 * (shared ? L.Is : L.I) + BN - 1) / BN : H / BN) - 1);
   // Weight block of the group: its expert index, or its cache slot.
   const int gw = (!PERSIST && slot_map && !shared) ? uni(slot_map[g]) : g;
   const int kdim = GATE_UP ? H : (shared ? L.Is : L.I);
@@ -210,7 +220,7 @@ __global__ __launch_bounds__((TileShape<BM, NW>::kThreads), (TileShape<BM, NW>::
     const int gch = ((lane & 7) ^ lds_swizzle(r)) * 8;
     const int row = m0 + min(r, rows_here - 1);         // rows past the group repeat its last row
     if (GATE_UP) {
-      const int tok = shared ? row : slot_tok[seg0 + row];
+      const int tok = shared ? row : min(max(slot_tok[seg0 + row], 0), T - 1);
       a_src[j] = x + (size_t)tok * H + gch;
     } else {
       a_src[j] = shared ? w.h_sh + (size_t)row * L.Is + gch : w.h + (size_t)(seg0 + row) * L.I + gch;
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(int T, int H, int K, Work w
 #pragma unroll
   for (int k = 0; k <= kMaxK; ++k) {
     if (k < K) {
-      row[k] = (size_t)w.slot_of[(size_t)t * K + k];
+      row[k] = (size_t)min(max(w.slot_of[(size_t)t * K + k], 0), T * K - 1);   // (clamped: see the GEMMs)
       sc[k] = w.topk_w[(size_t)t * K + k];
     } else {
       row[k] = (size_t)T * K + t;
@@ -557,7 +567,7 @@ hipError_t launch_gate_up(const LayerArgs& L, const bf16_t* x, int T, const Work
   auto k = gemm_kernel_for<true>(L, T, persist);
   const unsigned grid = persist ? (unsigned)(8 * ((std::max(num_cus, 8) + 7) / 8)) : gemm_grid(bound, unit);
   hipLaunchKernelGGL(k, dim3(grid), dim3(gemm_threads(L, T, true)), 0, s, L, x, T, w, (const int*)w.tiles_gu,
-                     (const int4*)w.tdesc_gu, (const int*)w.slot_tok, window, slot_map, unit);
+                     (const int4*)w.tdesc_gu, (const int*)w.slot_tok, window, slot_map, unit, (int)bound);
   return hipGetLastError();
 }
 
@@ -577,7 +587,8 @@ hipError_t launch_down(const LayerArgs& L, int T, const Work& w, int num_cus, hi
   }
   auto k = gemm_kernel_for<false>(L, T, false);
   hipLaunchKernelGGL(k, dim3(gemm_grid(bound, unit)), dim3(gemm_threads(L, T, false)), 0, s, L, (const bf16_t*)nullptr, T, w,
-                     (const int*)w.tiles_dn, (const int4*)w.tdesc_dn, (const int*)w.slot_tok, window, slot_map, unit);
+                     (const int*)w.tiles_dn, (const int4*)w.tdesc_dn, (const int*)w.slot_tok, window, slot_map, unit,
+                     (int)bound);
   return hipGetLastError();
 }
 

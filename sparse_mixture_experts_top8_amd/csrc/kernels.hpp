@@ -160,6 +160,18 @@ hipError_t launch_ranks(const void* logits, int dtype, int R, int E, int32_t* ra
 hipError_t launch_load_balance(const LayerArgs& L, int T, const Work& w, float* lb, float* mean_prob,
                                int32_t* counts, hipStream_t s);
 hipError_t launch_dispatch(const LayerArgs& L, int T, const Work& w, hipStream_t s);
+// Fused small-batch route (T <= kRouteMaxT, H <= 2048): router logits, top-K
+// selection and the per-group dispatch in one launch whose workgroups hand
+// data to each other through the workspace's tagged exchange region (w.lt)
+// with bounded waits; the same outputs as launch_router + launch_dispatch
+// (block histograms and probability sums aside, which it does not form).
+constexpr int kRouteMaxT = 64;
+constexpr int kRouteSelStride = kRouteMaxT * 8;   // words between the copies of the published selections
+__host__ __device__ inline bool route_fused_fits(int64_t T, int H, int K) {
+  return T >= 1 && T <= kRouteMaxT && H <= 2048 && H % 128 == 0 && K <= 8;
+}
+hipError_t launch_route_fused(const LayerArgs& L, const bf16_t* x, int T, const Work& w, float* logits_out,
+                              unsigned long long wait_ticks, hipStream_t s);
 // window (optional): int4 {first routed tile, count, first shared tile, count}
 // selecting part of the dispatch tile list; slot_map (optional): expert ->
 // weight block index (cache slot) for the routed groups.

@@ -69,6 +69,8 @@ constexpr size_t kCtlBytes = align256_c((size_t)moe::kDecodeCtlWords * 4);
 constexpr size_t kLogitTagBytes =
     align256_c((size_t)moe::kDecodeReplicas * (size_t)(moe::kDecodeMaxT * 256 + 64) * 8);
 constexpr size_t kControlRegionBytes = kCtlBytes + kLogitTagBytes;
+static_assert(kLogitTagBytes >= ((size_t)moe::kRouteMaxT * 256 + (size_t)moe::kDecodeReplicas * moe::kRouteSelStride) * 8,
+              "the tagged region holds the fused route's logits and selection copies");
 static_assert(moe::kDecodeMaxT * 256 + 64 == 16 * 256 + 64, "tagged-logit region sized for the largest fused batch");
 
 // Workspace layout, each region 256-byte aligned.  With base == nullptr only
@@ -84,7 +86,7 @@ Carve carve(const moe_layer_t* L, int64_t T, char* base) {
   };
   Carve c{};
   c.w.ctl = (uint32_t*)take(kCtlBytes);
-  take(kLogitTagBytes);
+  c.w.lt = (uint64_t*)take(kLogitTagBytes);
   c.w.topk_idx = (int32_t*)take(tk * 4);
   c.w.topk_w = (float*)take(tk * 4);
   c.w.gate_s = (float*)take(t * 4);
@@ -276,6 +278,26 @@ moe::Work grouped_work(const moe_layer_t* L, int64_t T, void* ws) {
   return w;
 }
 
+// Router and dispatch of the grouped path: one fused launch for small
+// batches (its bounded waits report through the control block like the
+// fused decode path's), else the router kernels, then the dispatch kernels.
+// between() runs after the router (a phase mark of the traced forward).
+template <typename Between>
+int route_dispatch(const moe::LayerArgs& a, const bf16_t* x, int t, const moe::Work& w, float* logits,
+                   hipStream_t s, Between between) {
+  int rc;
+  if (moe::route_fused_fits(t, a.H, a.K)) {
+    if ((rc = launch_status(moe::launch_route_fused(a, x, t, w, logits, g_wait_ticks.load(std::memory_order_relaxed), s),
+                            "route")) != MOE_OK)
+      return rc;
+    return between();
+  }
+  if ((rc = launch_status(moe::launch_router(a, x, t, w, logits, s), "router")) != MOE_OK) return rc;
+  if ((rc = between()) != MOE_OK) return rc;
+  return launch_status(moe::launch_dispatch(a, t, w, s), "dispatch");
+}
+int no_mark() { return MOE_OK; }
+
 }  // namespace
 
 extern "C" {
@@ -339,8 +361,7 @@ int moe_route(const moe_layer_t* L, const void* x, int64_t T, int32_t* topk_idx,
   if (shared_gate) w.gate_s = shared_gate;
   const moe::LayerArgs a = layer_args(L);
   hipStream_t s = (hipStream_t)stream;
-  if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, (int)T, w, logits, s), "router")) != MOE_OK) return rc;
-  return launch_status(moe::launch_dispatch(a, (int)T, w, s), "dispatch");
+  return route_dispatch(a, (const bf16_t*)x, (int)T, w, logits, s, no_mark);
 }
 
 int moe_load_balance(const moe_layer_t* L, const void* x, int64_t T, float* lb, float* mean_prob,
@@ -409,9 +430,7 @@ int forward_impl(const moe_layer_t* L, const void* x, int64_t T, void* out, void
       return rc;
     xin = w.xn;
   }
-  if ((rc = launch_status(moe::launch_router(a, xin, t, w, nullptr, s), "router")) != MOE_OK) return rc;
-  if ((rc = mark(1)) != MOE_OK) return rc;
-  if ((rc = launch_status(moe::launch_dispatch(a, t, w, s), "dispatch")) != MOE_OK) return rc;
+  if ((rc = route_dispatch(a, xin, t, w, nullptr, s, [&] { return mark(1); })) != MOE_OK) return rc;
   if ((rc = mark(2)) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_gate_up(a, xin, t, w, cus, s), "gate_up")) != MOE_OK) return rc;
   if ((rc = mark(3)) != MOE_OK) return rc;
@@ -558,6 +577,9 @@ int moe_forward_streamed(const moe_layer_t* L, const void* x, int64_t T, void* o
   char* slot_dn = slot_gu + (size_t)C * gu;
   hipStream_t s = (hipStream_t)stream;
   const int t = (int)T;
+  // The separate router kernels (no cross-workgroup waits), whose routing the
+  // fused route reproduces bit for bit: the stream plan and the slot map
+  // trust the dispatch tables.
   if ((rc = launch_status(moe::launch_router(a, (const bf16_t*)x, t, w, nullptr, s), "router")) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_dispatch(a, t, w, s), "dispatch")) != MOE_OK) return rc;
   if ((rc = launch_status(moe::launch_stream_plan(a, w, (int)C, (int)R, s), "stream plan")) != MOE_OK) return rc;

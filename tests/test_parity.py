@@ -112,7 +112,8 @@ def check_output(xb, bits, dims, gi, out_rows, rows, tag):
 
 def call_status(ws):
     """moe_workspace_status of the latest call made with ws: 0, or
-    MOE_ERR_TIMEOUT if a wait inside the fused decode kernel gave up."""
+    MOE_ERR_TIMEOUT if a wait inside the fused decode kernel or the fused
+    small-batch route gave up."""
     return _moe().workspace_status(ws)
 
 
@@ -399,12 +400,17 @@ def test_decode_timeout_is_reported(full):
     # right.  With the budget restored the next call on the same workspace
     # reports MOE_OK and is right, and so does a grouped-path call after a
     # timed-out one.
+    # The fused route of 17..64 tokens has the same bounded waits (logits to
+    # selection, selections to dispatch); after a give-up its workgroups may
+    # write dispatch tables from different views of the selections, which the
+    # GEMMs and the combine read through clamped indices.  A batch of 65
+    # tokens takes the separate router kernels, which do not wait.
     moe = _moe()
     d, bits, layer, _, _ = full
-    ws = layer.workspace(17)
+    ws = layer.workspace(65)
     timed_out = 0
-    for T in (1, 16):
-        _say(f"case full decode forced timeout T={T}")
+    for T in (1, 16, 17, 64):
+        _say(f"case full decode / fused route forced timeout T={T}")
         x = moe.bits_to_device(mi.make_x(d, T, 9990 + T), "cuda")
         good = moe.forward(x, layer, ws=ws)
         assert moe.workspace_status(ws) == 0
@@ -429,12 +435,12 @@ def test_decode_timeout_is_reported(full):
     try:
         moe.forward(moe.bits_to_device(mi.make_x(d, 16, 9995), "cuda"), layer, ws=ws)
         st16 = moe.workspace_status(ws)
-        moe.forward(moe.bits_to_device(mi.make_x(d, 17, 9996), "cuda"), layer, ws=ws)
-        st17 = moe.workspace_status(ws)
+        moe.forward(moe.bits_to_device(mi.make_x(d, 65, 9996), "cuda"), layer, ws=ws)
+        st65 = moe.workspace_status(ws)
     finally:
         moe.set_wait_budget_us(prev)
-    _say(f"forced timeouts: {timed_out} of 6 fused calls; then fused {st16}, grouped {st17}")
-    assert st17 == 0, "a grouped-path call reports the status of its own call"
+    _say(f"forced timeouts: {timed_out} of 12 calls with waits; then fused {st16}, separate router {st65}")
+    assert st65 == 0, "a call without waits reports the status of its own call"
 
 
 def test_full_decode_identical_tokens(full):
@@ -817,6 +823,9 @@ def test_toy_streamed(toy, toy_host, T, cap):
     torch.cuda.synchronize()
     gi = check_routing(xb, bits, d, r, f"toy streamed T={T}")
     check_output(xb, bits, d, gi, _np(got.float()), np.arange(T), f"toy streamed T={T} slots={cap}")
+    # The streamed path routes with the separate router kernels, the resident
+    # path of 17..64 tokens with the fused route: equal bits also check that
+    # both compute the same routing.
     if T > 16:
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), "streamed != resident"
 
@@ -965,8 +974,8 @@ def test_full_workspace_sized_for_largest_batch(full):
         x = moe.bits_to_device(mi.make_x(d, T, 9600 + T), "cuda")
         a = moe.forward(x, layer, ws=big)
         torch.cuda.synchronize()
-        if T <= 16:
-            assert call_status(big) == 0, "decode path wait timed out"
+        if T <= 64:
+            assert call_status(big) == 0, "fused path wait timed out"
         b = moe.forward(x, layer)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"T={T}"
