@@ -249,7 +249,7 @@ def _source_ok(rec):
     import hashlib
     csrc = os.path.join(ROOT, "sparse_mixture_experts_top8_amd", "csrc")
     h = hashlib.sha256()
-    for f in (rec["source"], "common.hpp", "kernels.hpp", "lds_pipe.hpp"):
+    for f in (rec["source"], "common.hpp", "kernels.hpp", "lds_pipe.hpp", "handoff.hpp", "group_dispatch.hpp"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16] == rec["source_sha"]
 
