@@ -744,15 +744,17 @@ def test_full_bf16_logits(full, T):
     check_output_bf16(xb, bits, gi, _np(out.float()), np.arange(T), f"full bf16 T={T}")
 
 
-def test_full_bf16_logits_skewed(full):
-    # Scores of size ~50 have a bf16 spacing of 0.25: ties are frequent.
+@pytest.mark.parametrize("T", [64, 2048])
+def test_full_bf16_logits_skewed(full, T):
+    # Scores of size ~50 have a bf16 spacing of 0.25: ties are frequent.  64
+    # tokens take the fused route, 2048 the separate router kernels.
     d, _, _, zb, zlayer = full
     wl = mi.WORKLOADS["zipf16384"]
-    xb = mi.workload_x(wl)[:2048]
-    _say("case full bf16 logits, skewed router, T=2048")
+    xb = mi.workload_x(wl)[:T]
+    _say(f"case full bf16 logits, skewed router, T={T}")
     r, out = run_layer(zlayer.with_logits_bf16(), xb, want_logits=True)
-    gi = check_routing_bf16(xb, zb, d, r, "skewed bf16 T=2048")
-    check_output_bf16(xb, zb, gi, _np(out.float()), np.arange(2048), "skewed bf16 T=2048")
+    gi = check_routing_bf16(xb, zb, d, r, f"skewed bf16 T={T}")
+    check_output_bf16(xb, zb, gi, _np(out.float()), np.arange(T), f"skewed bf16 T={T}")
 
 
 @pytest.mark.parametrize("E,R", [(1, 3), (7, 5), (16, 1000), (64, 9), (255, 33), (256, 4096)])
