@@ -46,7 +46,8 @@ constexpr int kSmallT = 256;             // up to this many tokens: 32-token log
 constexpr int kLargeT = 8192;            // from this many tokens: 128-token logits tiles (the router is
                                          // read half as often; zipf16384 router 90 -> 80 us, while at
                                          // 4096 tokens the extra H slices cost more than that saves)
-constexpr int kColBlocks = 5;            // column blocks per wave (17 for E = 256, plus the gate column)
+constexpr int kColBlocks = 5;            // column blocks per wave of four (17 for E = 256, plus the gate column)
+constexpr int kMaxSub = 17;              // column blocks of 16 for E <= 256 plus the gate column
 constexpr int kDepth = 2;                // 64-wide k-steps in flight per wave (router_logits_kernel)
 constexpr int kMaxRouterCols = 260;      // router_cols(256)
 
@@ -155,23 +156,32 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
 // itself, the four waves' copies met only in the 32 KB L1 (a deeper register
 // ring was slower: zipf16384 router 78 -> 87 us).  Per accumulator the MFMAs
 // run in the same k order, so the sums are the same.
-template <int kTB>
-__global__ __launch_bounds__(256, 1) void router_logits_lds_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
+//
+// Waves per workgroup of the LDS-staged logits kernel: eight for 64-token
+// tiles (two per SIMD, each with at most three column blocks; 200 registers
+// instead of 304: prefill4096 router phase 28.0-28.4 -> 27.0-27.9 us), four
+// otherwise (32-token tiles give eight waves no whole direct-to-LDS load per
+// step; 128-token tiles would spill).
+constexpr int router_lds_waves(int tb) { return tb == 4 ? 8 : 4; }
+
+template <int kTB, int kNW = router_lds_waves(kTB)>
+__global__ __launch_bounds__(64 * kNW, 1) void router_logits_lds_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
                                                                   int ksplit, float* __restrict__ part,
                                                                   int* __restrict__ hist_zero, int hist_n,
                                                                   uint32_t* __restrict__ ctl, uint32_t tag) {
   using namespace pipe;
   constexpr int NS = 4;
   constexpr int kRows = 16 * kTB, kStage = kRows * 128;
-  constexpr int kDma = kRows * 8 / 256;              // direct-to-LDS instructions per wave per step
-  constexpr int kVm = kDma + 2 * kColBlocks;         // loads per wave per step
+  constexpr int kCB = (kMaxSub + kNW - 1) / kNW;     // column blocks per wave
+  constexpr int kDma = kRows * 8 / (64 * kNW);       // direct-to-LDS instructions per wave per step
+  constexpr int kVm = kDma + 2 * kCB;                // loads per wave per step
   static_assert(kDma >= 1 && 3 * kVm <= 63, "x rows and router rows per step");
   __shared__ __attribute__((aligned(1024))) char lds[NS * kStage];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (ctl && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) ctl[kCtlLast] = tag;
   if (hist_zero) {
     const int nwg = gridDim.x * gridDim.y, wg = blockIdx.y * gridDim.x + blockIdx.x;
-    for (int i = wg * 256 + tid; i < hist_n; i += nwg * 256) hist_zero[i] = 0;
+    for (int i = wg * (64 * kNW) + tid; i < hist_n; i += nwg * (64 * kNW)) hist_zero[i] = 0;
   }
   const int t0 = blockIdx.x * kRows, s = blockIdx.y;
   const int H = L.H, E = L.E, Ep = router_cols(E);
@@ -182,48 +192,48 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds_kernel(LayerArgs L, 
   const int nsteps = ((nk + NS - 1) / NS) * NS;     // padded to the ring; padding steps add nothing
   const uint32_t lds_base = (uint32_t)(size_t)(lds_ptr_t)lds;
 
-  // x rows: instruction j of wave w writes row 8 (4 j + w) + lane / 8 of a
+  // x rows: instruction j of wave w writes row 8 (kNW j + w) + lane / 8 of a
   // stage, stored chunk lane % 8 holding chunk (lane % 8) ^ swz(row); rows
   // past T repeat row T - 1 (their outputs are dropped).
   const bf16_t* a_src[kDma];
 #pragma unroll
   for (int j = 0; j < kDma; ++j) {
-    const int r = 8 * (4 * j + wv) + (lane >> 3);
+    const int r = 8 * (kNW * j + wv) + (lane >> 3);
     a_src[j] = x + (size_t)min(t0 + r, T - 1) * H + kbeg + ((lane & 7) ^ lds_swizzle(r)) * 8;
   }
-  // Router rows of the wave's column blocks wave + 4 jj (rows past E + 1
+  // Router rows of the wave's column blocks wave + kNW jj (rows past E + 1
   // repeat row E; blocks past the last are loaded, not used, so every wave
   // issues the same loads); lane quarter q reads elements 16 q .. 16 q + 15.
-  const bf16_t* brow[kColBlocks];
+  const bf16_t* brow[kCB];
 #pragma unroll
-  for (int jj = 0; jj < kColBlocks; ++jj) {
-    const int e = min(16 * (wv + 4 * jj) + r16, E);
+  for (int jj = 0; jj < kCB; ++jj) {
+    const int e = min(16 * (wv + kNW * jj) + r16, E);
     brow[jj] = (e < E ? L.router_w + (size_t)e * H : L.sh_expert_gate) + kbeg + 16 * q;
   }
-  u32x4 wb[NS][kColBlocks][2];
-  auto issue = [&](u32x4 (&wbs)[kColBlocks][2], int st, int ks) {
+  u32x4 wb[NS][kCB][2];
+  auto issue = [&](u32x4 (&wbs)[kCB][2], int st, int ks) {
     const int kv = min(ks, nk - 1);
 #pragma unroll
     for (int j = 0; j < kDma; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + 64 * kv), (lds_ptr_t)(lds + st * kStage + 1024 * (4 * j + wv)),
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[j] + 64 * kv), (lds_ptr_t)(lds + st * kStage + 1024 * (kNW * j + wv)),
                                        16, 0, 0);
 #pragma unroll
-    for (int jj = 0; jj < kColBlocks; ++jj)
+    for (int jj = 0; jj < kCB; ++jj)
 #pragma unroll
       for (int h = 0; h < 2; ++h) wbs[jj][h] = ld16(brow[jj] + 64 * kv + 8 * h);
   };
-  f32x4 acc[kTB][kColBlocks];
+  f32x4 acc[kTB][kCB];
 #pragma unroll
   for (int i = 0; i < kTB; ++i)
 #pragma unroll
-    for (int jj = 0; jj < kColBlocks; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < kCB; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   issue(wb[0], 0, 0);
   issue(wb[1], 1, 1);
   issue(wb[2], 2, 2);
   // One k-step (YOUNGER: steps already requested after this one; ISSUE:
   // whether it requests step ks + 3), as in grouped_gemm_kernel.
-  auto step = [&](auto younger_c, auto issue_c, u32x4 (&wcur)[kColBlocks][2], u32x4 (&wnext)[kColBlocks][2], int st,
+  auto step = [&](auto younger_c, auto issue_c, u32x4 (&wcur)[kCB][2], u32x4 (&wnext)[kCB][2], int st,
                   int ks) {
     wait_vm<decltype(younger_c)::value * kVm>();
     barrier();
@@ -236,14 +246,14 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds_kernel(LayerArgs L, 
       lds_read_group<0>(Y, sa1, std::make_integer_sequence<int, kTB>{});
       wait_lds_keep<kTB>(X);
 #pragma unroll
-      for (int jj = 0; jj < kColBlocks; ++jj)
-        if (wv + 4 * jj < nsub)
+      for (int jj = 0; jj < kCB; ++jj)
+        if (wv + kNW * jj < nsub)
 #pragma unroll
           for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(X[i], wcur[jj][0], acc[i][jj]);
       wait_lds_keep<0>(Y);
 #pragma unroll
-      for (int jj = 0; jj < kColBlocks; ++jj)
-        if (wv + 4 * jj < nsub)
+      for (int jj = 0; jj < kCB; ++jj)
+        if (wv + kNW * jj < nsub)
 #pragma unroll
           for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(Y[i], wcur[jj][1], acc[i][jj]);
     }
@@ -268,9 +278,9 @@ __global__ __launch_bounds__(256, 1) void router_logits_lds_kernel(LayerArgs L, 
   // D[4 (lane / 16) + r][lane % 16] of each 16 x 16 block.
   float* out = part + (size_t)s * T * Ep;
 #pragma unroll
-  for (int jj = 0; jj < kColBlocks; ++jj) {
-    const int e = 16 * (wv + 4 * jj) + r16;
-    if (wv + 4 * jj < nsub && e <= E) {
+  for (int jj = 0; jj < kCB; ++jj) {
+    const int e = 16 * (wv + kNW * jj) + r16;
+    if (wv + kNW * jj < nsub && e <= E) {
 #pragma unroll
       for (int i = 0; i < kTB; ++i)
 #pragma unroll
@@ -564,13 +574,13 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
     hipLaunchKernelGGL(router_logits_kernel<1>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
                        w.call_tag);
   else if (tile == 32)
-    hipLaunchKernelGGL(router_logits_lds_kernel<2>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+    hipLaunchKernelGGL(router_logits_lds_kernel<2>, grid, dim3(64 * router_lds_waves(2)), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
                        w.call_tag);
   else if (tile == 64)
-    hipLaunchKernelGGL(router_logits_lds_kernel<4>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+    hipLaunchKernelGGL(router_logits_lds_kernel<4>, grid, dim3(64 * router_lds_waves(4)), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
                        w.call_tag);
   else
-    hipLaunchKernelGGL(router_logits_lds_kernel<8>, grid, dim3(256), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
+    hipLaunchKernelGGL(router_logits_lds_kernel<8>, grid, dim3(64 * router_lds_waves(8)), 0, s, L, x, T, ks, w.rlog, hz, hn, w.ctl,
                        w.call_tag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
