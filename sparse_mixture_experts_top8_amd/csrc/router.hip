@@ -157,12 +157,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(LayerArgs L, const b
 // ring was slower: zipf16384 router 78 -> 87 us).  Per accumulator the MFMAs
 // run in the same k order, so the sums are the same.
 //
-// Waves per workgroup of the LDS-staged logits kernel: eight for 64-token
-// tiles (two per SIMD, each with at most three column blocks; 200 registers
-// instead of 304: prefill4096 router phase 28.0-28.4 -> 27.0-27.9 us), four
-// otherwise (32-token tiles give eight waves no whole direct-to-LDS load per
-// step; 128-token tiles would spill).
-constexpr int router_lds_waves(int tb) { return tb == 4 ? 8 : 4; }
+// Waves per workgroup of the LDS-staged logits kernel: eight for 64- and
+// 128-token tiles (two per SIMD, each with at most three column blocks;
+// 200 registers instead of 304 at 64 tokens, prefill4096 router phase
+// 28.0-28.4 -> 27.0-27.9 us; 252 instead of 420 at 128 tokens, with one
+// operand array for both k halves, zipf16384 58.1-59.0 -> 52.9-54.0 us),
+// four for 32-token tiles (which give eight waves no whole direct-to-LDS
+// load per step).
+constexpr int router_lds_waves(int tb) { return tb >= 4 ? 8 : 4; }
 
 template <int kTB, int kNW = router_lds_waves(kTB)>
 __global__ __launch_bounds__(64 * kNW, 1) void router_logits_lds_kernel(LayerArgs L, const bf16_t* __restrict__ x, int T,
@@ -241,21 +243,41 @@ __global__ __launch_bounds__(64 * kNW, 1) void router_logits_lds_kernel(LayerArg
     if (ks < nk) {
       const uint32_t sa0 = lds_base + st * kStage + r16 * 128 + (((2 * q) ^ lds_swizzle(r16)) << 4);
       const uint32_t sa1 = lds_base + st * kStage + r16 * 128 + (((2 * q + 1) ^ lds_swizzle(r16)) << 4);
-      u32x4 X[kTB], Y[kTB];
-      lds_read_group<0>(X, sa0, std::make_integer_sequence<int, kTB>{});
-      lds_read_group<0>(Y, sa1, std::make_integer_sequence<int, kTB>{});
-      wait_lds_keep<kTB>(X);
+      if constexpr (kNW == 8 && kTB == 8) {
+        // One operand array for both k halves (two waves per SIMD cover the
+        // reads' latency; a second array would not fit in 256 registers).
+        u32x4 X[kTB];
+        lds_read_group<0>(X, sa0, std::make_integer_sequence<int, kTB>{});
+        wait_lds_keep<0>(X);
 #pragma unroll
-      for (int jj = 0; jj < kCB; ++jj)
-        if (wv + kNW * jj < nsub)
+        for (int jj = 0; jj < kCB; ++jj)
+          if (wv + kNW * jj < nsub)
 #pragma unroll
-          for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(X[i], wcur[jj][0], acc[i][jj]);
-      wait_lds_keep<0>(Y);
+            for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(X[i], wcur[jj][0], acc[i][jj]);
+        lds_read_group<0>(X, sa1, std::make_integer_sequence<int, kTB>{});
+        wait_lds_keep<0>(X);
 #pragma unroll
-      for (int jj = 0; jj < kCB; ++jj)
-        if (wv + kNW * jj < nsub)
+        for (int jj = 0; jj < kCB; ++jj)
+          if (wv + kNW * jj < nsub)
 #pragma unroll
-          for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(Y[i], wcur[jj][1], acc[i][jj]);
+            for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(X[i], wcur[jj][1], acc[i][jj]);
+      } else {
+        u32x4 X[kTB], Y[kTB];
+        lds_read_group<0>(X, sa0, std::make_integer_sequence<int, kTB>{});
+        lds_read_group<0>(Y, sa1, std::make_integer_sequence<int, kTB>{});
+        wait_lds_keep<kTB>(X);
+#pragma unroll
+        for (int jj = 0; jj < kCB; ++jj)
+          if (wv + kNW * jj < nsub)
+#pragma unroll
+            for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(X[i], wcur[jj][0], acc[i][jj]);
+        wait_lds_keep<0>(Y);
+#pragma unroll
+        for (int jj = 0; jj < kCB; ++jj)
+          if (wv + kNW * jj < nsub)
+#pragma unroll
+            for (int i = 0; i < kTB; ++i) acc[i][jj] = mfma16(Y[i], wcur[jj][1], acc[i][jj]);
+      }
     }
   };
   using c0 = std::integral_constant<int, 0>;
