@@ -122,19 +122,25 @@ __device__ void dispatch_tiles(LayerArgs L, int T, const Work& w, int g, const i
   }
 }
 
-// Stable scatter of router block blk's pairs (at most 32*K <= 256).
+// Stable scatter of router block blk's pairs (at most 32*K <= 256).  A
+// token's K experts are distinct, so a pair's rank among the block's pairs of
+// its expert is the number of the block's earlier tokens that chose that
+// expert: the population of the expert's token mask below its token.
 __device__ void dispatch_scatter(LayerArgs L, int T, const Work& w, int blk, const int* s_off) {
-  __shared__ int keys[256];
+  static_assert(kRouterTokens == 32, "one 32-bit token mask per expert");
+  __shared__ uint32_t mask[256];
   const int E = L.E, K = L.K;
   const int j = threadIdx.x;
   const int q0 = blk * kRouterTokens * K;
   const int n = min(kRouterTokens * K, T * K - q0);
-  const int key = j < n ? w.topk_idx[q0 + j] : -1;
-  keys[j] = key;
+  const int key = j < n ? min(max(w.topk_idx[q0 + j], 0), E - 1) : 0;
+  const int tl = j / K;
+  mask[j] = 0u;   // E <= 256 = the block size
+  __syncthreads();
+  if (j < n) atomicOr(&mask[key], 1u << tl);
   __syncthreads();
   if (j < n) {
-    int rank = 0;
-    for (int i = 0; i < j; ++i) rank += (keys[i] == key);
+    const int rank = __popc(mask[key] & ((1u << tl) - 1u));
     const int slot = s_off[key] + w.blk_counts[(size_t)blk * E + key] + rank;
     w.perm[slot] = q0 + j;
     w.slot_of[q0 + j] = slot;
