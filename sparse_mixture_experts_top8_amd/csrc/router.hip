@@ -422,6 +422,8 @@ __global__ __launch_bounds__(kSelWaves * 64) void router_select_kernel(LayerArgs
 // results are the same bit for bit.  For the multi-launch dispatch
 // (block_hist) each selected pair is counted into its router block's
 // histogram, which the logits kernel zeroed.
+// kS: an upper bound of ksplit (the slice registers are sized by it).
+template <int kS>
 __global__ __launch_bounds__(256) void router_select_tok_kernel(LayerArgs L, int T, int ksplit,
                                                                 const float* __restrict__ part, Work w,
                                                                 float* __restrict__ logits_out, int block_hist) {
@@ -432,10 +434,10 @@ __global__ __launch_bounds__(256) void router_select_tok_kernel(LayerArgs L, int
   const float* src = part + (size_t)t * Ep;
   const size_t sstride = (size_t)T * Ep;
   const bool have = 4 * lane < Ep;
-  u32x4 q[kMaxSlices];
-  float g[kMaxSlices];
+  u32x4 q[kS];
+  float g[kS];
 #pragma unroll
-  for (int i = 0; i < kMaxSlices; ++i)
+  for (int i = 0; i < kS; ++i)
     if (i < ksplit) {
       q[i] = have ? ld16(src + i * sstride + 4 * lane) : u32x4{0u, 0u, 0u, 0u};
       g[i] = src[i * sstride + E];
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(256) void router_select_tok_kernel(LayerArgs L, int
   float lv[1][4] = {{0.f, 0.f, 0.f, 0.f}};
   float zg = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxSlices; ++i)
+  for (int i = 0; i < kS; ++i)
     if (i < ksplit) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) lv[0][c] += __uint_as_float(q[i][c]);
@@ -606,9 +608,14 @@ hipError_t launch_router(const LayerArgs& L, const bf16_t* x, int T, const Work&
                        w.call_tag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (per_token)
-    hipLaunchKernelGGL(router_select_tok_kernel, dim3((T + 3) / 4), dim3(256), 0, s, L, T, ks, (const float*)w.rlog,
-                       w, logits_out, block_hist ? 1 : 0);
+  if (per_token) {
+    // The slice registers sized for the split in use: fewer registers, more
+    // waves per SIMD (two slices: 18 VGPRs instead of 90, zipf16384 router
+    // phase 52.7-54.0 -> 50.9-52.2 us; four: 60).
+    auto k = ks <= 2 ? router_select_tok_kernel<2> : ks <= 4 ? router_select_tok_kernel<4> : router_select_tok_kernel<kMaxSlices>;
+    hipLaunchKernelGGL(k, dim3((T + 3) / 4), dim3(256), 0, s, L, T, ks, (const float*)w.rlog, w, logits_out,
+                       block_hist ? 1 : 0);
+  }
   else
     hipLaunchKernelGGL(router_select_kernel, dim3(router_blocks(T)), dim3(kSelWaves * 64), 0, s, L, T, ks,
                        (const float*)w.rlog, w, logits_out, psum_out);
