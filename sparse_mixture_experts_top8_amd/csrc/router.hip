@@ -16,7 +16,8 @@
 // Logits: one workgroup per (64-token tile, or 16- or 32-token tile for small
 // batches and 128-token tile for large ones, slice of H); the shared gate row
 // rides along as column E, so the E + 1 columns are 17 MFMA column blocks of
-// 16.  Each wave owns column blocks w, w + 4, ... and streams their router rows
+// 16.  Wave w of n owns column blocks w, w + n, ... (n = 4, or 8 for the
+// LDS-staged kernel's 64- and 128-token tiles) and streams their router rows
 // through registers in 64-wide k-steps (each row's whole 128-byte line per
 // step), writing fp32 partial sums (one fp32 accumulator chain of at most
 // H / 32 MFMAs per slice).  The tile's x rows go to LDS once per k-step and
@@ -25,6 +26,7 @@
 // large batches the router is read once per 64 or 128 tokens through L2.
 // Small batches split H into up to H/64 slices so that the launch still spans
 // the chip.
+//
 // Selection, two kernels.
 // router_select_kernel (for the load-balance statistic, which needs its
 // per-block probability sums): one workgroup of 16 waves per 32 tokens sums
